@@ -1,0 +1,180 @@
+"""Seeded synthetic inputs for the causal GQA attention path.
+
+This module draws inputs only; it holds none of the attention arithmetic and is
+shared by the test suite, the benchmark and the fp64 reference.  Every array is
+produced by ``numpy.random.default_rng(seed)`` (PCG64): standard normal values
+drawn in float32 in the order Q, K, V and rounded to fp16 (round to nearest
+even).  Shapes follow the workloads of the pages:
+
+* causal prefill -- Hq=6 query heads sharing Hkv=1 K/V head, D=256, scale 1/16,
+  Q rows at the last positions of the key range ("[Kernel][SM70] Default
+  long-prefill GQA architecture", Purpose: Q=8000, KV=40000..128000 step 8000).
+* paged block-sparse prefill -- 4096 query rows, page-16 cache behind a
+  non-monotonic page table, 64-row query blocks selecting 4-token KV blocks,
+  selections of 64 / 512 / 2048 tokens, partial tails of 0..3 tokens ("[Kernel]
+  [SM70] Repair #378 on latest main", Changes and Test Result).
+* FP8 verifier tail -- 2..8 query rows at the end of a 261888-token context with
+  K/V stored as OCP E4M3 codes and one fp32 scale per tensor ("[Perf] Ship the
+  qualified SM70 long-context layout...", Changes and Measurement).  The E4M3
+  codes are produced with torch's float8_e4m3fn cast (round to nearest even)
+  of value/scale with scale = amax/448.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+
+import numpy as np
+
+HQ, HKV, D = 6, 1, 256
+SCALE = 1.0 / 16.0
+
+
+def _normal16(rng, shape):
+    return rng.standard_normal(shape, dtype=np.float32).astype(np.float16)
+
+
+# ---------------------------------------------------------------- causal prefill
+@dataclass(frozen=True)
+class CausalConfig:
+    name: str
+    nq: int
+    n_kv: int
+    hq: int = HQ
+    hkv: int = HKV
+    d: int = D
+    scale: float = SCALE
+
+    @property
+    def q_pos0(self) -> int:
+        return self.n_kv - self.nq
+
+
+TINY = CausalConfig("tiny_q256_kv1024", nq=256, n_kv=1024)
+LONG_40K = CausalConfig("long_q8000_kv40000", nq=8000, n_kv=40000)
+SWEEP = tuple(CausalConfig(f"long_q8000_kv{kv}", nq=8000, n_kv=kv) for kv in range(48000, 128001, 8000))
+HEADLINE = SWEEP[-1]  # Q=8000, KV=128000
+
+
+def causal_inputs(nq: int, n_kv: int, seed: int, hq: int = HQ, hkv: int = HKV, d: int = D):
+    """q [nq, hq, d], k [n_kv, hkv, d], v [n_kv, hkv, d] as fp16 numpy arrays."""
+    rng = np.random.default_rng(seed)
+    q = _normal16(rng, (nq, hq, d))
+    k = _normal16(rng, (n_kv, hkv, d))
+    v = _normal16(rng, (n_kv, hkv, d))
+    return q, k, v
+
+
+# ------------------------------------------------------- paged block-sparse prefill
+PAGE_SIZE = 16
+KV_BLOCK_TOKENS = 4
+QBLOCK_ROWS = 64
+PAGE_POOL = 512
+
+
+@dataclass
+class PagedSparseInputs:
+    q: np.ndarray            # fp16 [nq, hq, d]
+    k_cache: np.ndarray      # fp16 [n_pages, page_size, hkv, d]
+    v_cache: np.ndarray
+    page_table: np.ndarray   # int32 [n_table]
+    qblock_offsets: np.ndarray  # int32 [n_qblocks + 1]
+    kv_block_ids: np.ndarray    # int32 [offsets[-1]]
+    q_pos0: int
+    live_len: int
+    page_size: int = PAGE_SIZE
+    kv_block_tokens: int = KV_BLOCK_TOKENS
+    qblock_rows: int = QBLOCK_ROWS
+    scale: float = SCALE
+    meta: dict = field(default_factory=dict)
+
+
+def paged_sparse_inputs(select_tokens: int, tail: int, seed: int, nq: int = 4096, n_pages: int = PAGE_POOL,
+                        poison_stale: bool = False, saturate: bool = False, identity_table: bool = False,
+                        hq: int = HQ, hkv: int = HKV, d: int = D) -> PagedSparseInputs:
+    """Paged block-sparse prefill inputs.
+
+    Query row r sits at position tail + r, so the request holds ``tail`` tokens
+    of earlier context and live_len = tail + nq.  The page table maps the
+    ceil(live_len / 16) logical pages to distinct physical pages drawn as a
+    seeded random permutation of the pool (non-monotonic).  Query block b (rows
+    64b..64b+63) always selects the 4-token block holding the position of its
+    last row (its causal-diagonal block, of which only part may be visible: the
+    partial tail), plus min(select_tokens/4 - 1, diag) distinct random earlier
+    blocks (all earlier blocks when ``saturate``), emitted in shuffled order.
+    With ``poison_stale`` every cache slot that holds no live token is NaN.
+    """
+    if select_tokens % KV_BLOCK_TOKENS or select_tokens < KV_BLOCK_TOKENS:
+        raise ValueError("selection must be a positive multiple of the block size")
+    rng = np.random.default_rng(seed)
+    q = _normal16(rng, (nq, hq, d))
+    k_cache = _normal16(rng, (n_pages, PAGE_SIZE, hkv, d))
+    v_cache = _normal16(rng, (n_pages, PAGE_SIZE, hkv, d))
+    live_len = tail + nq
+    n_table = -(-live_len // PAGE_SIZE)
+    if n_table > n_pages:
+        raise ValueError("page pool too small")
+    perm = rng.permutation(n_pages)
+    page_table = (np.arange(n_table) if identity_table else perm[:n_table]).astype(np.int32)
+    if poison_stale:
+        live = np.zeros((n_pages, PAGE_SIZE), dtype=bool)
+        toks = np.arange(live_len)
+        live[page_table[toks // PAGE_SIZE], toks % PAGE_SIZE] = True
+        k_cache[~live] = np.float16(np.nan)
+        v_cache[~live] = np.float16(np.nan)
+    n_qblocks = -(-nq // QBLOCK_ROWS)
+    offsets = [0]
+    ids = []
+    for b in range(n_qblocks):
+        last_pos = tail + min(nq, (b + 1) * QBLOCK_ROWS) - 1
+        diag = last_pos // KV_BLOCK_TOKENS
+        n_extra = diag if saturate else min(select_tokens // KV_BLOCK_TOKENS - 1, diag)
+        extra = rng.choice(diag, size=n_extra, replace=False) if n_extra > 0 else np.zeros(0, dtype=np.int64)
+        sel = np.concatenate([[diag], extra]).astype(np.int64)
+        rng.shuffle(sel)
+        ids.append(sel)
+        offsets.append(offsets[-1] + sel.size)
+    return PagedSparseInputs(
+        q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
+        qblock_offsets=np.asarray(offsets, dtype=np.int32),
+        kv_block_ids=np.concatenate(ids).astype(np.int32),
+        q_pos0=tail, live_len=live_len,
+        meta=dict(select_tokens=select_tokens, tail=tail, seed=seed, nq=nq, n_pages=n_pages,
+                  poison_stale=poison_stale, saturate=saturate),
+    )
+
+
+# ------------------------------------------------------------ FP8 verifier tail
+VERIFY_CONTEXT = 261888
+E4M3_MAX = 448.0
+
+
+@dataclass
+class VerifyInputs:
+    q: np.ndarray        # fp16 [nq, hq, d]
+    k_bytes: np.ndarray  # uint8 [L, hkv, d]
+    v_bytes: np.ndarray
+    k_scale: float
+    v_scale: float
+    scale: float = SCALE
+
+
+def _to_e4m3(x: np.ndarray, scale: np.float32) -> np.ndarray:
+    import torch  # the float8 cast is a library primitive used only to make inputs
+
+    y = np.clip(x / scale, -E4M3_MAX, E4M3_MAX).astype(np.float32)
+    return torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def verify_inputs(nq: int, context: int, seed: int, hq: int = HQ, hkv: int = HKV, d: int = D) -> VerifyInputs:
+    """Verifier-tail inputs: fp16 Q and E4M3-coded K/V from N(0,1) draws."""
+    rng = np.random.default_rng(seed)
+    q = _normal16(rng, (nq, hq, d))
+    kf = rng.standard_normal((context, hkv, d), dtype=np.float32)
+    vf = rng.standard_normal((context, hkv, d), dtype=np.float32)
+    k_scale = np.float32(np.abs(kf).max() / np.float32(E4M3_MAX))
+    v_scale = np.float32(np.abs(vf).max() / np.float32(E4M3_MAX))
+    kb = _to_e4m3(kf, k_scale)
+    del kf
+    vb = _to_e4m3(vf, v_scale)
+    return VerifyInputs(q=q, k_bytes=kb, v_bytes=vb, k_scale=float(k_scale), v_scale=float(v_scale))
