@@ -1,0 +1,385 @@
+// Dense causal GQA prefill for gfx950: fused S^T = K Q^T, online softmax and
+// O^T += V^T P^T on the matrix cores, split evenly over the compute units with
+// an exact log-sum-exp merge.
+//
+// The operation is the causal FP16 long-prefill of the long-prefill page
+// ("[Kernel][SM70] Default long-prefill GQA architecture", Purpose): six query
+// heads sharing one K/V head at D = 256, packed so that every K/V fragment is
+// used by all six heads, with per-tile (max, sum, accumulator) states merged
+// exactly.  That page's V100 design (separate QK and PV Tensor-Core GEMMs
+// through a 750-MiB score workspace) is not followed: scores never leave the
+// registers.
+//
+// Workgroup: 4 waves (one per SIMD) x 64 packed rows = 256 rows (a q-block).
+// Each wave keeps its 64 rows of Q as matrix-core B fragments in registers
+// (2 column blocks of 32 rows x 16 steps of 16 head-dim columns) and its
+// O^T accumulator (2 x 8 tiles of 32x32 fp32).  K/V tiles of 64 keys stream
+// HBM -> LDS by direct-to-LDS loads into a double buffer (2 x 64 KiB).
+#include "attn_common.hpp"
+#include "prefill_sched.hpp"
+#include "launch.hpp"
+
+#include <type_traits>
+
+namespace gqa {
+
+namespace {
+
+constexpr int kTileBytes = kTileKeys * kRowBytes;  // 32 KiB per K or V tile
+// Rows per wave = 32 * kPrefillC, waves per workgroup = kPrefillW.
+#ifndef GQA_PREFILL_C
+#define GQA_PREFILL_C 1
+#endif
+constexpr int kPrefillC = GQA_PREFILL_C;
+constexpr int kPrefillW = 8 / kPrefillC;
+
+struct PrefillParams {
+  const _Float16* q;
+  const _Float16* k;
+  const _Float16* v;
+  _Float16* o;
+  float* part;
+  long long total;
+  int nrows;
+  int kv_live;  // keys 0 .. kv_live-1 can be visible (q_pos0 + nq)
+  int q_pos0;
+  int nqb;
+  int grid;
+  uint32_t part_bytes;
+  float c;  // scale * log2(e): scores are kept in log2 units
+};
+
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+
+// Stage keys tile*64 .. tile*64+63 of K and V into LDS.  With W waves, wave w
+// copies rows (64/W)w .. (64/W)(w+1)-1: 32/W copies of 1 KiB (two rows) for K
+// and as many for V.  Rows past the last key read as zeros (buffer range
+// check); they lie after every query position, so they are always masked.
+//
+// Lane l of copy i fills physical chunk l%32 of row r = (64/W)w + 2i + l/32,
+// so it fetches the logical chunk that the swizzle puts there.  With
+// x = r % 16 = (2i + l/32) % 16 (64/W is a multiple of 16 for W <= 4, and for
+// W = 8 the wave's first row is a multiple of 8, which the V swizzle only
+// needs), the byte offset from the wave's first row is
+// 2i*512 + l/32*512 + 16*(l%32 ^ swz(r)): for K, swz(r) = r % 16 gives
+// (kl ^ 32(i + 4*(w%2 when W=8))) + 1024i ... computed below per copy.
+template <int W>
+__device__ __forceinline__ void issue_tile(rsrc_t rk, rsrc_t rv, int tile, char* kdst, char* vdst, int wave,
+                                           uint32_t kl, uint32_t vl) {
+  constexpr int kRowsPerWave = kTileKeys / W;
+  constexpr int kCopies = kRowsPerWave / 2;
+  const uint32_t soff = (uint32_t)tile * (kTileKeys * kRowBytes) + (uint32_t)wave * (kRowsPerWave * kRowBytes);
+  // copy i covers rows r0 = kRowsPerWave*wave + 2i (+1); its index within the
+  // 16-row swizzle period is j = (r0 % 16) / 2
+  const int jbase = (kRowsPerWave * wave % 16) / 2;
+#pragma unroll
+  for (int i = 0; i < kCopies; ++i) {
+    const int r0 = kRowsPerWave * wave + 2 * i;
+    const uint32_t j = (uint32_t)(jbase + i);  // < 8
+    load_lds_16B(rk, (GQA_LDS char*)(kdst + r0 * kRowBytes), kl ^ (32u * j), soff + 1024u * i);
+    load_lds_16B(rv, (GQA_LDS char*)(vdst + r0 * kRowBytes), vl ^ (128u * (j & 3)), soff + 1024u * i);
+  }
+}
+
+// Partial slot layout (fp32): acc[64 column quads][256 rows][4], m[256], l[256].
+constexpr int kPartM = kRowsPerBlock * kHeadDim;
+constexpr int kPartL = kPartM + kRowsPerBlock;
+
+// One piece of work: tiles tile_lo .. tile_hi-1 of q-block b, with W waves
+// of 32*C packed rows each (32*C*W = 256).
+template <int C, int W>
+__device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem, int b, int tile_lo, int tile_hi,
+                                              bool full, int slot) {
+  constexpr int kRowsPerWave = 32 * C;
+  static_assert(kRowsPerWave * W == kRowsPerBlock, "a workgroup covers one q-block");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const uint32_t kl = 512u * half + 16u * (uint32_t)(col ^ half);
+  const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
+
+  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
+  // keys after the last query position never take part: they read as zeros
+  const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes);
+  const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes);
+
+  const int row_base = b * kRowsPerBlock + wave * kRowsPerWave;
+  const bool wave_active = row_base < p.nrows;
+  const int wrow_hi = min(row_base + kRowsPerWave - 1, p.nrows - 1);
+  const int wpos_lo = p.q_pos0 + row_base / kGroup;
+  const int wpos_hi = p.q_pos0 + wrow_hi / kGroup;
+
+  int pos[C];
+  h8 qf[C][16];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    const int row = row_base + 32 * c + col;
+    pos[c] = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
+    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[c][s] = load_16B(rq, qoff + s * 32);
+  }
+
+  f16x acc[C][8];
+#pragma unroll
+  for (int c = 0; c < C; ++c)
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[c][dt] = f16x{};
+  float m[C], l[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) {
+    m[c] = -INFINITY;
+    l[c] = 0.f;
+  }
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
+
+  // LDS: V buffers at 0 and 32 KiB, K buffers at 64 and 96 KiB (every
+  // fragment offset then fits the 16-bit immediate of the LDS read).
+  uint32_t bk = k_lane_base(lane);
+  uint32_t bv = v_lane_base(lane);
+
+  issue_tile<W>(rk, rv, tile_lo, smem + 2 * kTileBytes, smem, wave, kl, vl);
+  wait_vmem();
+  __syncthreads();
+
+  auto step = [&](auto bufc, int tile) {
+    constexpr int BUF = decltype(bufc)::value;
+    if (tile + 1 < tile_hi)
+      issue_tile<W>(rk, rv, tile + 1, smem + (2 + (BUF ^ 1)) * kTileBytes, smem + (BUF ^ 1) * kTileBytes, wave, kl,
+                    vl);
+    const GQA_LDS char* kt = (const GQA_LDS char*)smem + (2 + BUF) * kTileBytes;
+    const GQA_LDS char* vt = (const GQA_LDS char*)smem + BUF * kTileBytes;
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k0 = tile * kTileKeys + 32 * kb;
+      if (!wave_active || k0 > wpos_hi) continue;  // every key of this block is in the future
+      const bool need_mask = k0 + 31 > wpos_lo;
+
+      // S^T[32 keys][32C rows] = K Q^T over the 256 head-dim columns.
+      f16x s[C];
+#pragma unroll
+      for (int c = 0; c < C; ++c) s[c] = f16x{};
+#pragma unroll
+      for (int si = 0; si < 16; ++si) {
+        const h8 a = read_k_frag(kt, bk, kb, si);
+#pragma unroll
+        for (int c = 0; c < C; ++c) s[c] = mfma(a, qf[c][si], s[c]);
+      }
+
+      // Online softmax in log2 units; this lane holds 16 keys of one row.
+      h8 pk[C][2];
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+        if (need_mask) {
+#pragma unroll
+          for (int vv = 0; vv < 16; ++vv) {
+            const int key = k0 + 8 * (vv >> 2) + 4 * half + (vv & 3);
+            s[c][vv] = key <= pos[c] ? s[c][vv] : -INFINITY;
+          }
+        }
+        float mx = s[c][0];
+#pragma unroll
+        for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[c][vv]);
+        mx = swap_halves_max(mx);
+        const float tmax = mx * p.c;
+        if (__any(tmax > m[c] + kRescaleTau)) {
+          const float mnew = fmaxf(m[c], tmax);
+          const float alpha = (mnew == -INFINITY) ? 1.0f : fast_exp2(m[c] - mnew);
+          m[c] = mnew;
+          l[c] *= alpha;
+#pragma unroll
+          for (int dt = 0; dt < 8; ++dt) acc[c][dt] *= alpha;
+        }
+        const float msub = (m[c] == -INFINITY) ? 0.0f : m[c];
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          float e[8];
+#pragma unroll
+          for (int u = 0; u < 8; ++u) e[u] = fast_exp2(__builtin_fmaf(s[c][8 * t + u], p.c, -msub));
+          const h2 p0 = cvt2(e[0], e[1]);
+          const h2 p1 = cvt2(e[2], e[3]);
+          const h2 p2 = cvt2(e[4], e[5]);
+          const h2 p3 = cvt2(e[6], e[7]);
+          // the row sum is taken over the fp16 weights that multiply V
+          float ls = l[c];
+          ls = __builtin_amdgcn_fdot2(p0, ones, ls, false);
+          ls = __builtin_amdgcn_fdot2(p1, ones, ls, false);
+          ls = __builtin_amdgcn_fdot2(p2, ones, ls, false);
+          ls = __builtin_amdgcn_fdot2(p3, ones, ls, false);
+          l[c] = ls;
+          pk[c][t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        }
+      }
+
+      // O^T[256 d][32C rows] += V^T[256 d][32 keys] P^T[32 keys][32C rows].
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt) {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int key0 = 32 * kb + 16 * t;
+          const h8 a = cat_h4(read_vt_half(vt, bv, key0, dt), read_vt_half(vt, bv, key0 + 8, dt));
+#pragma unroll
+          for (int c = 0; c < C; ++c) acc[c][dt] = mfma(a, pk[c][t], acc[c][dt]);
+        }
+      }
+    }
+    wait_vmem();
+    __syncthreads();
+  };
+
+  for (int tile = tile_lo; tile < tile_hi; tile += 2) {
+    step(std::integral_constant<int, 0>{}, tile);
+    if (tile + 1 < tile_hi) step(std::integral_constant<int, 1>{}, tile + 1);
+  }
+
+  float lt[C];
+#pragma unroll
+  for (int c = 0; c < C; ++c) lt[c] = swap_halves_sum(l[c]);
+
+  if (full) {
+    // Normalised fp16 rows; rows past the last one are dropped by the range check.
+    const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const float inv = lt[c] > 0.f ? 1.0f / lt[c] : 0.f;
+      const uint32_t obase = (uint32_t)(row_base + 32 * c + col) * kRowBytes + half * 8;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const h2 lo = cvt2(acc[c][dt][4 * g + 0] * inv, acc[c][dt][4 * g + 1] * inv);
+          const h2 hi = cvt2(acc[c][dt][4 * g + 2] * inv, acc[c][dt][4 * g + 3] * inv);
+          store_8B(ro, obase + (32 * dt + 8 * g) * 2, h4{lo[0], lo[1], hi[0], hi[1]});
+        }
+    }
+  } else {
+    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+    const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
+#pragma unroll
+    for (int c = 0; c < C; ++c) {
+      const int rl = wave * kRowsPerWave + 32 * c + col;
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int quad = 8 * dt + 2 * g + half;  // columns 4*quad .. 4*quad+3
+          const f4 x = {acc[c][dt][4 * g], acc[c][dt][4 * g + 1], acc[c][dt][4 * g + 2], acc[c][dt][4 * g + 3]};
+          store_16B(rp, sbase + (uint32_t)((quad * kRowsPerBlock + rl) * 16), __builtin_bit_cast(u4, x));
+        }
+      if (half == 0) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[c]), rp, sbase + (kPartM + rl) * 4, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt[c]), rp, sbase + (kPartL + rl) * 4, 0, 0);
+      }
+    }
+  }
+}
+
+template <int C, int W>
+__global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
+  const int w = blockIdx.x;
+  long long t0 = prefill_range_start(w, p.total, p.grid);
+  const long long t1 = prefill_range_start(w + 1, p.total, p.grid);
+  if (t0 >= t1) return;
+  int b = 0;
+  long long cb = 0;
+  for (;;) {
+    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+    if (cb + nt > t0) break;
+    cb += nt;
+    ++b;
+  }
+  while (t0 < t1) {
+    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+    const long long seg_end = cb + nt < t1 ? cb + nt : t1;
+    const int lo = (int)(t0 - cb), hi = (int)(seg_end - cb);
+    prefill_piece<C, W>(p, smem, b, lo, hi, lo == 0 && hi == nt, w + b);
+    t0 = seg_end;
+    cb += nt;
+    ++b;
+  }
+}
+
+// Exact merge of the partials of q-blocks that were split across workgroups:
+// M = max_k m_k, O = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
+// Workgroup (b, quarter): 64 rows of q-block b; thread (row, 64 columns).
+__global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
+  const int b = blockIdx.x >> 2;
+  const int quarter = blockIdx.x & 3;
+  long long cb = 0;
+  for (int i = 0; i < b; ++i) cb += prefill_block_tiles(i, p.nrows, p.q_pos0);
+  const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+  const int w0 = prefill_owner(cb, p.total, p.grid);
+  const int w1 = prefill_owner(cb + nt - 1, p.total, p.grid);
+  if (w0 == w1) return;  // done whole by one workgroup, already written
+  const int tid = threadIdx.x;
+  const int rl = quarter * 64 + (tid & 63);
+  const int dq = tid >> 6;  // columns 64*dq .. 64*dq+63
+  const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+  float M = -INFINITY;
+  for (int w = w0; w <= w1; ++w) {
+    const uint32_t sb = (uint32_t)(w + b) * (uint32_t)(kPartialFloats * 4);
+    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0)));
+  }
+  f4 o[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int w = w0; w <= w1; ++w) {
+    const uint32_t sb = (uint32_t)(w + b) * (uint32_t)(kPartialFloats * 4);
+    const float mw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
+    const float lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
+    const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+    L += aw * lw;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((16 * dq + j) * kRowsPerBlock + rl) * 16), 0, 0);
+      o[j] += aw * __builtin_bit_cast(f4, x);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+  const uint32_t obase = (uint32_t)(b * kRowsPerBlock + rl) * kRowBytes + 128 * dq;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const h2 a0 = cvt2(o[j][0] * inv, o[j][1] * inv), a1 = cvt2(o[j][2] * inv, o[j][3] * inv);
+    const h2 b0 = cvt2(o[j + 1][0] * inv, o[j + 1][1] * inv), b1 = cvt2(o[j + 1][2] * inv, o[j + 1][3] * inv);
+    const h8 x = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    store_16B(ro, obase + j * 8, __builtin_bit_cast(u4, x));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* o, int nq, int n_kv, int q_pos0,
+                                 int hq, float scale, void* workspace, hipStream_t stream) {
+  const PrefillSched s = prefill_schedule(nq, hq, q_pos0);
+  PrefillParams p;
+  p.q = (const _Float16*)q;
+  p.k = (const _Float16*)k;
+  p.v = (const _Float16*)v;
+  p.o = (_Float16*)o;
+  p.part = (float*)workspace;
+  p.total = s.total;
+  p.nrows = s.nrows;
+  p.kv_live = q_pos0 + nq;
+  (void)n_kv;
+  p.q_pos0 = q_pos0;
+  p.nqb = s.nqb;
+  p.grid = s.grid;
+  p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
+  p.c = scale * kLog2e;
+  hipLaunchKernelGGL((prefill_causal_fwd<kPrefillC, kPrefillW>), dim3(s.grid), dim3(64 * kPrefillW), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (prefill_needs_merge(s)) {
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * 4), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace gqa

@@ -1,0 +1,91 @@
+// Work decomposition of the dense causal prefill, shared by host and device.
+//
+// Packed rows: Q [nq][6][256] is read as a [nq*6][256] matrix whose row
+// R = token*6 + head; all six heads of a token share the token's causal
+// position q_pos0 + R/6 and the one K/V head, so a block of packed rows is one
+// tall GEMM against each K/V tile (the head packing of the long-prefill page,
+// Purpose).
+//
+// A q-block is 256 consecutive packed rows (one workgroup, four waves of 64).
+// Its key range is 0 .. pmax (the position of its last row), cut into 64-key
+// tiles.  Laying the q-blocks' tiles end to end gives a line of T tiles that
+// is split evenly over G workgroups (workgroup w takes tiles floor(wT/G) ..
+// floor((w+1)T/G) - 1).  Where a workgroup's range cuts a q-block, each piece
+// leaves an online-softmax partial (max, sum, unnormalised accumulator) that a
+// second kernel merges exactly by log-sum-exp -- the block partial plus exact
+// merge of the long-prefill page, with the split chosen for an even load on
+// all compute units.  The piece of q-block b done by workgroup w is stored in
+// partial slot w + b (unique: walking the line, every new piece starts at a
+// workgroup boundary, a q-block boundary or both).
+#pragma once
+
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kRowsPerBlock = 256;  // packed rows per workgroup
+constexpr int kTileKeys = 64;       // keys per K/V tile
+constexpr int kTargetGrid = 256;    // one workgroup per MI355X compute unit
+constexpr int kMinTilesPerWG = 16;
+
+struct PrefillSched {
+  int nrows;        // nq * hq
+  int q_pos0;
+  int nqb;          // number of q-blocks
+  long long total;  // T
+  int grid;         // G
+};
+
+__host__ __device__ inline int prefill_block_tiles(int b, int nrows, int q_pos0) {
+  int last = (b + 1) * kRowsPerBlock - 1;
+  if (last > nrows - 1) last = nrows - 1;
+  const int pmax = q_pos0 + last / 6;
+  return (pmax + kTileKeys) / kTileKeys;  // ceil((pmax + 1) / 64)
+}
+
+// First tile of workgroup w's range.
+__host__ __device__ inline long long prefill_range_start(int w, long long total, int grid) {
+  return (long long)w * total / grid;
+}
+
+// Workgroup whose range contains tile x.
+__host__ __device__ inline int prefill_owner(long long x, long long total, int grid) {
+  return (int)(((x + 1) * grid - 1) / total);
+}
+
+inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
+  PrefillSched s;
+  s.nrows = nq * hq;
+  s.q_pos0 = q_pos0;
+  s.nqb = (s.nrows + kRowsPerBlock - 1) / kRowsPerBlock;
+  long long t = 0;
+  for (int b = 0; b < s.nqb; ++b) t += prefill_block_tiles(b, s.nrows, q_pos0);
+  s.total = t;
+  long long g = (t + kMinTilesPerWG - 1) / kMinTilesPerWG;
+  if (g < s.nqb) g = s.nqb;
+  if (g > kTargetGrid) g = kTargetGrid;
+  if (g > t) g = t;
+  s.grid = (int)g;
+  return s;
+}
+
+// Partial slot: fp32 O^T [256 d][256 rows], then m [256], then l [256].
+constexpr size_t kPartialFloats = (size_t)256 * 256 + 256 + 256;
+
+// True when some q-block is cut between workgroups (its partials need merging).
+inline bool prefill_needs_merge(const PrefillSched& s) {
+  long long cb = 0;
+  for (int b = 0; b < s.nqb; ++b) {
+    const int nt = prefill_block_tiles(b, s.nrows, s.q_pos0);
+    if (prefill_owner(cb, s.total, s.grid) != prefill_owner(cb + nt - 1, s.total, s.grid)) return true;
+    cb += nt;
+  }
+  return false;
+}
+
+inline size_t prefill_workspace_bytes(const PrefillSched& s) {
+  if (!prefill_needs_merge(s)) return 0;
+  return (size_t)(s.grid + s.nqb) * kPartialFloats * sizeof(float);
+}
+
+}  // namespace gqa

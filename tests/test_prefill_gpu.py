@@ -1,0 +1,72 @@
+"""GPU parity of gqa_prefill_causal against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import assert_parity, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+SCALE = workloads.SCALE
+
+
+def _gpu(q, k, v, q_pos0):
+    import gqa_causal_flash_amd as g
+
+    return to_host(g.gqa_prefill_causal(to_dev(q), to_dev(k), to_dev(v), q_pos0, SCALE))
+
+
+@pytest.mark.parametrize(
+    "nq,n_kv,q_pos0",
+    [
+        (256, 1024, 768),   # the tiny configuration
+        (1, 1, 0),          # one query, one key
+        (1, 200, 199),      # one query at the end
+        (7, 100, 93),       # ragged: 42 packed rows, partial tiles
+        (300, 300, 0),      # square causal from position 0
+        (64, 1000, 500),    # queries in the middle (keys after them exist)
+        (777, 2500, 1723),  # several q-blocks, ragged last block
+        (256, 40000, 39744),  # few q-blocks over a long key range: many splits, merge path
+    ],
+)
+def test_prefill_parity(nq, n_kv, q_pos0):
+    q, k, v = workloads.causal_inputs(nq, n_kv, seed=nq + n_kv)
+    out = _gpu(q, k, v, q_pos0)
+    ref, _ = oracle.prefill_causal(q, k, v, q_pos0, SCALE)
+    assert_parity(out, ref, f"nq={nq} n_kv={n_kv} q_pos0={q_pos0}")
+
+
+def test_prefill_ignores_keys_after_last_query():
+    """K/V rows after the last query position never take part (NaN there changes nothing)."""
+    nq, n_kv, q_pos0 = 100, 700, 300
+    q, k, v = workloads.causal_inputs(nq, n_kv, seed=5)
+    base = _gpu(q, k, v, q_pos0)
+    k2, v2 = k.copy(), v.copy()
+    k2[q_pos0 + nq:] = np.float16(np.nan)
+    v2[q_pos0 + nq:] = np.float16(np.nan)
+    out = _gpu(q, k2, v2, q_pos0)
+    assert np.isfinite(out).all()
+    assert np.array_equal(out, base)
+
+
+def test_prefill_deterministic():
+    nq, n_kv = 512, 9000
+    q, k, v = workloads.causal_inputs(nq, n_kv, seed=9)
+    a = _gpu(q, k, v, n_kv - nq)
+    b = _gpu(q, k, v, n_kv - nq)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("cfg", [workloads.LONG_40K, workloads.HEADLINE], ids=lambda c: c.name)
+def test_prefill_full_size_sampled_rows(cfg):
+    """Full-size long prefill in the benchmark's launch configuration, checked on sampled rows."""
+    q, k, v = workloads.causal_inputs(cfg.nq, cfg.n_kv, seed=0)
+    out = _gpu(q, k, v, cfg.q_pos0)
+    assert np.isfinite(out).all()
+    rng = np.random.default_rng(123)
+    rows = np.unique(np.concatenate([[0, 1, 42, 43, cfg.nq // 2, cfg.nq - 2, cfg.nq - 1],
+                                     rng.choice(cfg.nq, 57, replace=False)]))
+    ref, _ = oracle.prefill_causal(q, k, v, cfg.q_pos0, SCALE, rows=rows)
+    assert_parity(out[rows], ref, cfg.name)
