@@ -1,0 +1,197 @@
+#!/usr/bin/env python3
+"""Benchmark of libgqa on one MI355X.
+
+Default workload: dense causal GQA prefill, Q = 8000 query rows at positions
+120000..127999 of KV = 128000 keys, Hq = 6 query heads sharing Hkv = 1 K/V
+head, D = 256, scale 1/16, fp16 in / fp16 out with fp32 accumulation, seeded
+N(0,1) synthetic inputs resident in HBM.  One step is one gqa_prefill_causal
+call (main kernel + log-sum-exp merge).  The metric is algorithmic TFLOP/s:
+4 * D * Hq * (visible query-key pairs) per step over the measured step time.
+
+Prints ONE JSON line.  Besides the driver's fields it carries
+  roofline      the dominant kernel's achieved TFLOP/s (algorithmic FLOPs per
+                launch / its average duration, timed with HIP events recorded
+                by the library around that kernel on its stream) against the
+                fp16 dense matrix-core peak;
+  cpu_baseline  the fp64 oracle timed on this host's cores for a bounded sample
+                of query rows of the same workload, in the same unit;
+  paths         the same measurement for the other entry points (paged
+                block-sparse prefill, FP8 verifier tail) when they are built.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+PEAK_F16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
+PEAK_HBM_GBS = 8000.0
+# The long-prefill page's candidate at this workload (V100, FP16): 100.20284 ms.
+PAGE_MS_Q8000_KV128000 = 100.20284
+
+
+def prefill_flops(nq: int, n_kv: int, q_pos0: int, hq: int = 6, d: int = 256) -> float:
+    p0, p1 = q_pos0, q_pos0 + nq - 1
+    pairs = (p0 + 1 + p1 + 1) * nq // 2
+    return 4.0 * d * hq * pairs
+
+
+def _blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+
+        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
+        if n:
+            return int(max(n))
+    except Exception:
+        pass
+    return len(os.sched_getaffinity(0))
+
+
+def time_steps(fn, steps: int, warmup: int):
+    """Run fn warmup times, then time exactly `steps` calls (sync on both sides).
+
+    Returns (wall ms per step, main-kernel ms per launch from library events)."""
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    g.gqa_profile_start()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    kms, kn = g.gqa_profile_stop()
+    return wall, (kms / kn if kn else float("nan"))
+
+
+def bench_prefill(cfg, steps, warmup, seed=0):
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    q, k, v = workloads.causal_inputs(cfg.nq, cfg.n_kv, seed)
+    dq, dk, dv = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    o = torch.empty_like(dq)
+    nbytes = g.gqa_prefill_causal_workspace_size(cfg.nq, cfg.n_kv, cfg.q_pos0)
+    ws = torch.empty(max(nbytes, 1), dtype=torch.uint8, device="cuda")
+
+    def step():
+        g.gqa_prefill_causal(dq, dk, dv, cfg.q_pos0, cfg.scale, o=o, workspace=ws)
+
+    ms, kms = time_steps(step, steps, warmup)
+    flops = prefill_flops(cfg.nq, cfg.n_kv, cfg.q_pos0)
+    return dict(ms=ms, kernel_ms=kms, flops=flops, host=(q, k, v))
+
+
+def cpu_baseline_prefill(cfg, host, seconds: float):
+    """fp64 oracle on a sample of query rows spread over the workload, timed on this host."""
+    import oracle
+
+    q, k, v = host
+    rng = np.random.default_rng(7)
+
+    def run(n):
+        rows = np.sort(rng.choice(cfg.nq, n, replace=False))
+        t0 = time.perf_counter()
+        oracle.prefill_causal(q, k, v, cfg.q_pos0, cfg.scale, rows=rows)
+        dt = time.perf_counter() - t0
+        pairs = int((cfg.q_pos0 + rows + 1).sum())
+        return dt, pairs, n
+
+    n = 16
+    dt, pairs, n = run(n)
+    for _ in range(4):  # grow the sample until it takes about `seconds`
+        if dt >= 0.6 * seconds or n >= cfg.nq:
+            break
+        n = int(min(cfg.nq, max(2 * n, n * seconds / max(dt, 1e-3))))
+        dt, pairs, n = run(n)
+    flops = 4.0 * cfg.d * cfg.hq * pairs
+    return dict(
+        value=flops / dt / 1e12,
+        unit="TFLOP/s",
+        cores=_blas_threads(),
+        kind="oracle",
+        sample=f"{n} of {cfg.nq} query rows (x{cfg.hq} heads, all visible keys of each, up to {cfg.n_kv}) "
+               f"in {dt:.1f} s of fp64 numpy/BLAS",
+    )
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--kv", type=int, default=workloads.HEADLINE.n_kv, help="key count of the prefill workload")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print("bench.py: libgqa is a single-GPU library; this benchmark runs on exactly one GPU "
+              "(--gpus 1); a sharded multi-GPU run is not part of it.", file=sys.stderr)
+        return 2
+
+    import torch
+
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        return 1
+
+    cfg = workloads.CausalConfig(f"causal_gqa_prefill_q8000_kv{args.kv}", nq=8000, n_kv=args.kv)
+    r = bench_prefill(cfg, args.steps, args.warmup)
+    value = r["flops"] / (r["ms"] * 1e-3) / 1e12
+    achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+    line = {
+        "metric": "causal GQA prefill TFLOP/s & ms (Q=8000,KV=128K) + % of fp16 MFMA peak",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": round(PAGE_MS_Q8000_KV128000 / r["ms"], 3) if cfg.n_kv == 128000 else None,
+        "vs_baseline_note": "ratio to the long-prefill page's V100 candidate (100.20284 ms); context, not a target",
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "nq": cfg.nq, "n_kv": cfg.n_kv, "q_pos0": cfg.q_pos0, "hq": cfg.hq,
+                   "hkv": cfg.hkv, "d": cfg.d, "scale": cfg.scale, "seed": 0, "pct_of_fp16_peak":
+                   round(100 * value / PEAK_F16_TFLOPS, 2)},
+        "roofline": {
+            "kernel": "prefill_causal_fwd",
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_F16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+            "kernel_ms": round(r["kernel_ms"], 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline_prefill(cfg, r["host"], args.cpu_seconds)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -31,6 +31,8 @@ SIGNATURES = {
     "gqa_prefill_paged_sparse_dropped": (_i32, [_vp, _i32p, _vp]),
     "gqa_verify_fp8kv_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _szp]),
     "gqa_verify_fp8kv": (_i32, [_vp, _vp, _vp, _f32, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gqa_profile_start": (_i32, []),
+    "gqa_profile_stop": (_i32, [ctypes.POINTER(ctypes.c_double), _i32p]),
     "gqa_status_string": (ctypes.c_char_p, [_i32]),
     "gqa_last_hip_error": (ctypes.c_int, []),
     "gqa_abi_version": (ctypes.c_int, []),
@@ -131,4 +133,89 @@ def gqa_prefill_causal(q, k, v, q_pos0: int, scale: float, o=None, workspace=Non
                                   d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
                                   _stream(stream))
     _check(st, "gqa_prefill_causal")
+    return o
+
+
+# --------------------------------------------------------------- kernel timing
+def gqa_profile_start():
+    _check(lib().gqa_profile_start(), "gqa_profile_start")
+
+
+def gqa_profile_stop():
+    """(total_ms, count) of the main attention kernels launched since gqa_profile_start()."""
+    ms = ctypes.c_double(0.0)
+    n = ctypes.c_int32(0)
+    _check(lib().gqa_profile_stop(ctypes.byref(ms), ctypes.byref(n)), "gqa_profile_stop")
+    return ms.value, n.value
+
+
+# ------------------------------------------------------ paged block-sparse
+def gqa_prefill_paged_sparse_workspace_size(nq: int, n_block_ids: int, qblock_rows: int = 64, kv_block_tokens: int = 4,
+                                            hq: int = 6, hkv: int = 1, d: int = 256) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().gqa_prefill_paged_sparse_workspace_size(nq, n_block_ids, qblock_rows, kv_block_tokens, hq, hkv, d,
+                                                         ctypes.byref(out)), "gqa_prefill_paged_sparse_workspace_size")
+    return out.value
+
+
+def gqa_prefill_paged_sparse(q, k_cache, v_cache, page_table, qblock_offsets, kv_block_ids, q_pos0: int,
+                             live_len: int, scale: float, qblock_rows: int = 64, kv_block_tokens: int = 4, o=None,
+                             workspace=None, stream=None):
+    """Paged block-sparse causal prefill; caches [n_pages, page_size, Hkv, D] fp16, index arrays int32 on device."""
+    import torch
+
+    nq, hq, d = q.shape
+    n_pages, page_size, hkv, _ = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("k_cache and v_cache must have the same shape")
+    n_ids = kv_block_ids.numel()
+    if o is None:
+        o = torch.empty_like(q)
+    nbytes = gqa_prefill_paged_sparse_workspace_size(nq, n_ids, qblock_rows, kv_block_tokens, hq, hkv, d)
+    ws, ws_bytes = _workspace(nbytes, q.device, workspace)
+    st = lib().gqa_prefill_paged_sparse(
+        _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
+        _dev(page_table, torch.int32, "page_table"), page_table.numel(), n_pages, page_size,
+        _dev(qblock_offsets, torch.int32, "qblock_offsets"),
+        _dev(kv_block_ids, torch.int32, "kv_block_ids") if n_ids else None, n_ids, qblock_rows, kv_block_tokens, nq,
+        q_pos0, live_len, hq, hkv, d, scale, _dev(o, torch.float16, "o"),
+        None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream(stream))
+    _check(st, "gqa_prefill_paged_sparse")
+    return o, ws
+
+
+def gqa_prefill_paged_sparse_dropped(workspace, stream=None) -> int:
+    """Index entries the last paged call on `workspace` dropped as invalid (synchronises the stream)."""
+    n = ctypes.c_int32(0)
+    _check(lib().gqa_prefill_paged_sparse_dropped(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(n),
+                                                  _stream(stream)), "gqa_prefill_paged_sparse_dropped")
+    return n.value
+
+
+# ------------------------------------------------------------ FP8 verifier
+def gqa_verify_fp8kv_workspace_size(nq: int, n_kv: int, hq: int = 6, hkv: int = 1, d: int = 256) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().gqa_verify_fp8kv_workspace_size(nq, n_kv, hq, hkv, d, ctypes.byref(out)),
+           "gqa_verify_fp8kv_workspace_size")
+    return out.value
+
+
+def gqa_verify_fp8kv(q, k_e4m3, v_e4m3, k_scale: float, v_scale: float, scale: float, o=None, workspace=None,
+                     stream=None):
+    """Causal verifier tail: q [nq, Hq, D] fp16 at the last nq positions; k/v [n_kv, Hkv, D] uint8 E4M3 codes."""
+    import torch
+
+    nq, hq, d = q.shape
+    n_kv, hkv, _ = k_e4m3.shape
+    if tuple(v_e4m3.shape) != tuple(k_e4m3.shape):
+        raise ValueError("k and v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    nbytes = gqa_verify_fp8kv_workspace_size(nq, n_kv, hq, hkv, d)
+    ws, ws_bytes = _workspace(nbytes, q.device, workspace)
+    st = lib().gqa_verify_fp8kv(_dev(q, torch.float16, "q"), _dev(k_e4m3, torch.uint8, "k_e4m3"),
+                                _dev(v_e4m3, torch.uint8, "v_e4m3"), k_scale, v_scale, _dev(o, torch.float16, "o"), nq,
+                                n_kv, hq, hkv, d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()),
+                                ws_bytes, _stream(stream))
+    _check(st, "gqa_verify_fp8kv")
     return o

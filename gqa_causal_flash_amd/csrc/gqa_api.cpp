@@ -9,9 +9,12 @@
 
 #include <cmath>
 #include <cstdint>
+#include <vector>
 
 #include "launch.hpp"
+#include "paged_sched.hpp"
 #include "prefill_sched.hpp"
+#include "verify_sched.hpp"
 
 namespace {
 
@@ -48,9 +51,68 @@ gqa_status prefill_sizes(int32_t nq, int32_t n_kv, int32_t q_pos0, int32_t hq, i
   return GQA_OK;
 }
 
+struct Profiler {
+  bool on = false;
+  std::vector<hipEvent_t> pool;   // created events, reused across sessions
+  std::vector<hipEvent_t> marks;  // start/stop pairs of this session
+};
+thread_local Profiler g_prof;
+
+hipEvent_t prof_event() {
+  const size_t used = g_prof.marks.size();
+  if (used < g_prof.pool.size()) return g_prof.pool[used];
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  g_prof.pool.push_back(e);
+  return e;
+}
+
 }  // namespace
 
+namespace gqa {
+void prof_before(hipStream_t stream) {
+  if (!g_prof.on) return;
+  hipEvent_t e = prof_event();
+  if (e && hipEventRecord(e, stream) == hipSuccess) g_prof.marks.push_back(e);
+}
+void prof_after(hipStream_t stream) {
+  if (!g_prof.on || g_prof.marks.size() % 2 == 0) return;
+  hipEvent_t e = prof_event();
+  if (e && hipEventRecord(e, stream) == hipSuccess) {
+    g_prof.marks.push_back(e);
+  } else {
+    g_prof.marks.pop_back();  // drop the unmatched start
+  }
+}
+}  // namespace gqa
+
 extern "C" {
+
+gqa_status gqa_profile_start(void) {
+  g_prof.on = true;
+  g_prof.marks.clear();
+  return GQA_OK;
+}
+
+gqa_status gqa_profile_stop(double* total_ms, int32_t* count) {
+  if (!g_prof.on || !total_ms || !count) return GQA_ERR_INVALID;
+  g_prof.on = false;
+  double sum = 0.0;
+  int32_t n = 0;
+  for (size_t i = 0; i + 1 < g_prof.marks.size(); i += 2) {
+    hipError_t e = hipEventSynchronize(g_prof.marks[i + 1]);
+    if (e != hipSuccess) return hip_status(e);
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, g_prof.marks[i], g_prof.marks[i + 1]);
+    if (e != hipSuccess) return hip_status(e);
+    sum += ms;
+    ++n;
+  }
+  g_prof.marks.clear();
+  *total_ms = sum;
+  *count = n;
+  return GQA_OK;
+}
 
 const char* gqa_status_string(gqa_status status) {
   switch (status) {
@@ -91,6 +153,100 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
   if (need > 0 && (!workspace || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
   return hip_status(gqa::launch_prefill_causal(q, k, v, o, nq, n_kv, q_pos0, hq, scale, workspace,
                                                (hipStream_t)stream));
+}
+
+// ------------------------------------------------------- paged block-sparse
+namespace {
+gqa_status paged_sizes(int32_t nq, int32_t n_block_ids, int32_t qblock_rows, int32_t kv_block_tokens, int32_t hq,
+                       int32_t hkv, int32_t d) {
+  if (nq <= 0 || n_block_ids < 0 || qblock_rows <= 0 || kv_block_tokens <= 0) return GQA_ERR_INVALID;
+  gqa_status st = check_shape(hq, hkv, d);
+  if (st != GQA_OK) return st;
+  if (qblock_rows != gqa::kQBlockTokens || kv_block_tokens != gqa::kBlockTokens) return GQA_ERR_UNSUPPORTED;
+  if (!rows_fit((int64_t)nq * hq, 2 * d) || (int64_t)n_block_ids * 8 > kMaxBufferBytes) return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+}  // namespace
+
+gqa_status gqa_prefill_paged_sparse_workspace_size(int32_t nq, int32_t n_block_ids, int32_t qblock_rows,
+                                                   int32_t kv_block_tokens, int32_t hq, int32_t hkv, int32_t d,
+                                                   size_t* bytes) {
+  if (!bytes) return GQA_ERR_INVALID;
+  gqa_status st = paged_sizes(nq, n_block_ids, qblock_rows, kv_block_tokens, hq, hkv, d);
+  if (st != GQA_OK) return st;
+  const int nqb = (nq + gqa::kQBlockTokens - 1) / gqa::kQBlockTokens;
+  *bytes = gqa::paged_layout(nqb, n_block_ids).total;
+  return GQA_OK;
+}
+
+gqa_status gqa_prefill_paged_sparse(const void* q, const void* k_cache, const void* v_cache,
+                                    const int32_t* page_table, int32_t n_table, int32_t n_pages, int32_t page_size,
+                                    const int32_t* qblock_offsets, const int32_t* kv_block_ids, int32_t n_block_ids,
+                                    int32_t qblock_rows, int32_t kv_block_tokens, int32_t nq, int32_t q_pos0,
+                                    int32_t live_len, int32_t hq, int32_t hkv, int32_t d, float scale, void* o,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_cache || !v_cache || !page_table || !qblock_offsets || !o) return GQA_ERR_INVALID;
+  if (n_block_ids > 0 && !kv_block_ids) return GQA_ERR_INVALID;
+  if (!good_scale(scale)) return GQA_ERR_INVALID;
+  if (n_table <= 0 || n_pages <= 0 || page_size <= 0 || q_pos0 < 0 || live_len <= 0) return GQA_ERR_INVALID;
+  size_t need = 0;
+  gqa_status st = gqa_prefill_paged_sparse_workspace_size(nq, n_block_ids, qblock_rows, kv_block_tokens, hq, hkv, d,
+                                                          &need);
+  if (st != GQA_OK) return st;
+  if (page_size != gqa::kPageSize) return GQA_ERR_UNSUPPORTED;
+  if ((int64_t)q_pos0 + nq > live_len || (int64_t)live_len > (int64_t)n_table * page_size) return GQA_ERR_INVALID;
+  // the cache buffer plus the out-of-range marker offset must fit 32 bits
+  if ((int64_t)n_pages * page_size * hkv * d * 2 > 0xFFFFFF00ll) return GQA_ERR_UNSUPPORTED;
+  if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  return hip_status(gqa::launch_paged_sparse(q, k_cache, v_cache, page_table, n_table, n_pages, qblock_offsets,
+                                             kv_block_ids, n_block_ids, nq, q_pos0, live_len, hq, scale, o, workspace,
+                                             (hipStream_t)stream));
+}
+
+gqa_status gqa_prefill_paged_sparse_dropped(const void* workspace, int32_t* count, void* stream) {
+  if (!workspace || !count) return GQA_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t hdr[4] = {0, 0, 0, 0};
+  hipError_t e = hipMemcpyAsync(hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  if (hdr[0] != gqa::kPagedMagic || hdr[1] < 0) return GQA_ERR_INVALID;
+  const gqa::PagedLayout L = gqa::paged_layout(hdr[1], hdr[2]);
+  std::vector<int32_t> err((size_t)hdr[1]);
+  if (!err.empty()) {
+    e = hipMemcpyAsync(err.data(), (const char*)workspace + L.err, err.size() * 4, hipMemcpyDeviceToHost, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) return hip_status(e);
+  }
+  int64_t total = 0;
+  for (int32_t x : err) total += x;
+  *count = (int32_t)(total > 0x7FFFFFFF ? 0x7FFFFFFF : total);
+  return GQA_OK;
+}
+
+// ------------------------------------------------------------ FP8 verifier
+gqa_status gqa_verify_fp8kv_workspace_size(int32_t nq, int32_t n_kv, int32_t hq, int32_t hkv, int32_t d,
+                                           size_t* bytes) {
+  if (!bytes) return GQA_ERR_INVALID;
+  if (nq <= 0 || n_kv <= 0 || nq > n_kv) return GQA_ERR_INVALID;
+  gqa_status st = check_shape(hq, hkv, d);
+  if (st != GQA_OK) return st;
+  if (nq * hq > gqa::kVerifyMaxRows || n_kv > gqa::kVerifyMaxContext) return GQA_ERR_UNSUPPORTED;
+  *bytes = gqa::verify_workspace_bytes(gqa::verify_schedule(nq, n_kv, hq));
+  return GQA_OK;
+}
+
+gqa_status gqa_verify_fp8kv(const void* q, const uint8_t* k_e4m3, const uint8_t* v_e4m3, float k_scale,
+                            float v_scale, void* o, int32_t nq, int32_t n_kv, int32_t hq, int32_t hkv, int32_t d,
+                            float scale, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k_e4m3 || !v_e4m3 || !o) return GQA_ERR_INVALID;
+  if (!good_scale(scale) || !good_scale(k_scale) || !good_scale(v_scale)) return GQA_ERR_INVALID;
+  size_t need = 0;
+  gqa_status st = gqa_verify_fp8kv_workspace_size(nq, n_kv, hq, hkv, d, &need);
+  if (st != GQA_OK) return st;
+  if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  return hip_status(gqa::launch_verify_fp8kv(q, k_e4m3, v_e4m3, k_scale, v_scale, o, nq, n_kv, hq, scale, workspace,
+                                             (hipStream_t)stream));
 }
 
 }  // extern "C"

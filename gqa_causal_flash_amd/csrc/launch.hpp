@@ -9,7 +9,20 @@
 
 namespace gqa {
 
+// Kernel timing hook (see gqa_profile_start): the launchers bracket their main
+// attention kernel with these; both are no-ops unless profiling is on.
+void prof_before(hipStream_t stream);
+void prof_after(hipStream_t stream);
+
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* o, int nq, int n_kv, int q_pos0,
                                  int hq, float scale, void* workspace, hipStream_t stream);
+
+hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
+                               int n_table, int n_pages, const int32_t* qblock_offsets, const int32_t* kv_block_ids,
+                               int n_block_ids, int nq, int q_pos0, int live_len, int hq, float scale, void* o,
+                               void* workspace, hipStream_t stream);
+
+hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v, float k_scale, float v_scale,
+                               void* o, int nq, int n_kv, int hq, float scale, void* workspace, hipStream_t stream);
 
 }  // namespace gqa

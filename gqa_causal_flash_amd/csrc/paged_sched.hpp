@@ -1,0 +1,45 @@
+// Sizes and workspace layout of the paged block-sparse prefill (host + device).
+//
+// Query block b = 64 query tokens = 384 packed rows (token * 6 + head), handled
+// by three workgroups of 128 packed rows (4 waves x 32 rows).  Its selection
+// of 4-token KV blocks is translated, checked and sorted by physical address
+// by a prepass into the workspace:
+//
+//   int32 header[4]   {magic, number of query blocks, number of ids, 0}
+//   int32 err[nqb]    index entries of block b dropped as invalid
+//   int32 beg[nqb]    first entry of block b in `entries`
+//   int32 cnt[nqb]    number of entries of block b (sorted valid ones first)
+//   int2  entries[n_block_ids]  {first physical cache row, first logical token}
+//                                or {-1, INT32_MAX} for an entry that holds no
+//                                live token
+#pragma once
+
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gqa {
+
+constexpr int kPageSize = 16;
+constexpr int kBlockTokens = 4;
+constexpr int kQBlockTokens = 64;
+constexpr int kQBlockRows = kQBlockTokens * 6;  // 384 packed rows
+constexpr int kPagedRowsPerWG = 128;
+constexpr int kPagedWGsPerQBlock = kQBlockRows / kPagedRowsPerWG;  // 3
+constexpr int kPagedMagic = 0x47514150;  // "PAQG"
+constexpr int kSortMax = 2048;           // selections up to this many blocks are sorted
+
+struct PagedLayout {
+  size_t err, beg, cnt, entries, total;
+};
+
+inline PagedLayout paged_layout(int nqb, int n_ids) {
+  PagedLayout L;
+  L.err = 16;
+  L.beg = L.err + 4 * (size_t)nqb;
+  L.cnt = L.beg + 4 * (size_t)nqb;
+  L.entries = (L.cnt + 4 * (size_t)nqb + 15) / 16 * 16;
+  L.total = L.entries + 8 * (size_t)(n_ids > 0 ? n_ids : 1);
+  return L;
+}
+
+}  // namespace gqa

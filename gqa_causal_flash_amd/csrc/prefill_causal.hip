@@ -16,6 +16,7 @@
 // O^T accumulator (2 x 8 tiles of 32x32 fp32).  K/V tiles of 64 keys stream
 // HBM -> LDS by direct-to-LDS loads into a double buffer (2 x 64 KiB).
 #include "attn_common.hpp"
+#include "attn_tile.hpp"
 #include "prefill_sched.hpp"
 #include "launch.hpp"
 
@@ -133,7 +134,6 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
     m[c] = -INFINITY;
     l[c] = 0.f;
   }
-  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 
   // LDS: V buffers at 0 and 32 KiB, K buffers at 64 and 96 KiB (every
   // fragment offset then fits the 16-bit immediate of the LDS read).
@@ -156,75 +156,12 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
     for (int kb = 0; kb < 2; ++kb) {
       const int k0 = tile * kTileKeys + 32 * kb;
       if (!wave_active || k0 > wpos_hi) continue;  // every key of this block is in the future
-      const bool need_mask = k0 + 31 > wpos_lo;
-
-      // S^T[32 keys][32C rows] = K Q^T over the 256 head-dim columns.
-      f16x s[C];
-#pragma unroll
-      for (int c = 0; c < C; ++c) s[c] = f16x{};
-#pragma unroll
-      for (int si = 0; si < 16; ++si) {
-        const h8 a = read_k_frag(kt, bk, kb, si);
-#pragma unroll
-        for (int c = 0; c < C; ++c) s[c] = mfma(a, qf[c][si], s[c]);
-      }
-
-      // Online softmax in log2 units; this lane holds 16 keys of one row.
-      h8 pk[C][2];
-#pragma unroll
-      for (int c = 0; c < C; ++c) {
-        if (need_mask) {
-#pragma unroll
-          for (int vv = 0; vv < 16; ++vv) {
-            const int key = k0 + 8 * (vv >> 2) + 4 * half + (vv & 3);
-            s[c][vv] = key <= pos[c] ? s[c][vv] : -INFINITY;
-          }
-        }
-        float mx = s[c][0];
-#pragma unroll
-        for (int vv = 1; vv < 16; ++vv) mx = fmaxf(mx, s[c][vv]);
-        mx = swap_halves_max(mx);
-        const float tmax = mx * p.c;
-        if (__any(tmax > m[c] + kRescaleTau)) {
-          const float mnew = fmaxf(m[c], tmax);
-          const float alpha = (mnew == -INFINITY) ? 1.0f : fast_exp2(m[c] - mnew);
-          m[c] = mnew;
-          l[c] *= alpha;
-#pragma unroll
-          for (int dt = 0; dt < 8; ++dt) acc[c][dt] *= alpha;
-        }
-        const float msub = (m[c] == -INFINITY) ? 0.0f : m[c];
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          float e[8];
-#pragma unroll
-          for (int u = 0; u < 8; ++u) e[u] = fast_exp2(__builtin_fmaf(s[c][8 * t + u], p.c, -msub));
-          const h2 p0 = cvt2(e[0], e[1]);
-          const h2 p1 = cvt2(e[2], e[3]);
-          const h2 p2 = cvt2(e[4], e[5]);
-          const h2 p3 = cvt2(e[6], e[7]);
-          // the row sum is taken over the fp16 weights that multiply V
-          float ls = l[c];
-          ls = __builtin_amdgcn_fdot2(p0, ones, ls, false);
-          ls = __builtin_amdgcn_fdot2(p1, ones, ls, false);
-          ls = __builtin_amdgcn_fdot2(p2, ones, ls, false);
-          ls = __builtin_amdgcn_fdot2(p3, ones, ls, false);
-          l[c] = ls;
-          pk[c][t] = h8{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-        }
-      }
-
-      // O^T[256 d][32C rows] += V^T[256 d][32 keys] P^T[32 keys][32C rows].
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt) {
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int key0 = 32 * kb + 16 * t;
-          const h8 a = cat_h4(read_vt_half(vt, bv, key0, dt), read_vt_half(vt, bv, key0 + 8, dt));
-#pragma unroll
-          for (int c = 0; c < C; ++c) acc[c][dt] = mfma(a, pk[c][t], acc[c][dt]);
-        }
-      }
+      // keep the per-lane bases opaque so derived addresses are formed here,
+      // next to their use, instead of being hoisted and held in registers
+      asm volatile("" : "+v"(bk), "+v"(bv));
+      // mask only blocks that cross the causal diagonal of some row of the wave
+      attend_32keys<C>(kt, vt, bk, bv, kb, qf, acc, m, l, p.c, k0 + 31 > wpos_lo,
+                       [&](int c, int vv) { return k0 + lane_key(vv, half) <= pos[c]; });
     }
     wait_vmem();
     __syncthreads();
@@ -240,40 +177,15 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
   for (int c = 0; c < C; ++c) lt[c] = swap_halves_sum(l[c]);
 
   if (full) {
-    // Normalised fp16 rows; rows past the last one are dropped by the range check.
     const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const float inv = lt[c] > 0.f ? 1.0f / lt[c] : 0.f;
-      const uint32_t obase = (uint32_t)(row_base + 32 * c + col) * kRowBytes + half * 8;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const h2 lo = cvt2(acc[c][dt][4 * g + 0] * inv, acc[c][dt][4 * g + 1] * inv);
-          const h2 hi = cvt2(acc[c][dt][4 * g + 2] * inv, acc[c][dt][4 * g + 3] * inv);
-          store_8B(ro, obase + (32 * dt + 8 * g) * 2, h4{lo[0], lo[1], hi[0], hi[1]});
-        }
-    }
+    for (int c = 0; c < C; ++c) store_rows_f16(ro, row_base + 32 * c + col, half, acc[c], lt[c], 1.0f);
   } else {
     const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
     const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
 #pragma unroll
-    for (int c = 0; c < C; ++c) {
-      const int rl = wave * kRowsPerWave + 32 * c + col;
-#pragma unroll
-      for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int quad = 8 * dt + 2 * g + half;  // columns 4*quad .. 4*quad+3
-          const f4 x = {acc[c][dt][4 * g], acc[c][dt][4 * g + 1], acc[c][dt][4 * g + 2], acc[c][dt][4 * g + 3]};
-          store_16B(rp, sbase + (uint32_t)((quad * kRowsPerBlock + rl) * 16), __builtin_bit_cast(u4, x));
-        }
-      if (half == 0) {
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[c]), rp, sbase + (kPartM + rl) * 4, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt[c]), rp, sbase + (kPartL + rl) * 4, 0, 0);
-      }
-    }
+    for (int c = 0; c < C; ++c)
+      store_partial(rp, sbase, kRowsPerBlock, wave * kRowsPerWave + 32 * c + col, half, acc[c], m[c], lt[c]);
   }
 }
 
@@ -372,8 +284,10 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.grid = s.grid;
   p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
   p.c = scale * kLog2e;
+  prof_before(stream);
   hipLaunchKernelGGL((prefill_causal_fwd<kPrefillC, kPrefillW>), dim3(s.grid), dim3(64 * kPrefillW), 0, stream, p);
   hipError_t e = hipGetLastError();
+  prof_after(stream);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
     hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * 4), dim3(256), 0, stream, p);

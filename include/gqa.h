@@ -154,6 +154,21 @@ gqa_status gqa_verify_fp8kv(const void* q, const uint8_t* k_e4m3, const uint8_t*
                             float scale, void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Kernel timing (observability).
+ *
+ * Between gqa_profile_start() and gqa_profile_stop() on one host thread, every
+ * successful call made by that thread records a pair of HIP events on its
+ * stream around its main attention kernel (the one that reads K/V; merge and
+ * index kernels are excluded).  gqa_profile_stop() waits for those events and
+ * returns the summed kernel time in milliseconds and the number of kernels
+ * timed; it returns GQA_ERR_INVALID when profiling was not started.  This is
+ * the only state the library keeps between calls; it is per thread and holds
+ * HIP events only (no device memory).
+ * ------------------------------------------------------------------------ */
+gqa_status gqa_profile_start(void);
+gqa_status gqa_profile_stop(double* total_ms, int32_t* count);
+
+/* ------------------------------------------------------------------------ *
  * Utilities.
  * ------------------------------------------------------------------------ */
 /* Static, NUL-terminated description of a status code (never NULL). */

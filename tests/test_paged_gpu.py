@@ -1,0 +1,135 @@
+"""GPU parity of gqa_prefill_paged_sparse against the fp64 oracle (through the C ABI)."""
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from helpers import assert_parity, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+
+def _oracle(x, ids=None, offs=None, k_cache=None, v_cache=None, page_table=None):
+    return oracle.prefill_paged_sparse(
+        x.q, x.k_cache if k_cache is None else k_cache, x.v_cache if v_cache is None else v_cache,
+        x.page_table if page_table is None else page_table, x.page_size,
+        x.qblock_offsets if offs is None else offs, x.kv_block_ids if ids is None else ids, x.qblock_rows,
+        x.kv_block_tokens, x.q_pos0, x.live_len, x.scale)[0]
+
+
+def _gpu(x, ids=None, offs=None, k_cache=None, v_cache=None, page_table=None, want_ws=False):
+    import gqa_causal_flash_amd as g
+
+    out, ws = g.gqa_prefill_paged_sparse(
+        to_dev(x.q), to_dev(x.k_cache if k_cache is None else k_cache),
+        to_dev(x.v_cache if v_cache is None else v_cache), to_dev(x.page_table if page_table is None else page_table),
+        to_dev(x.qblock_offsets if offs is None else offs), to_dev(x.kv_block_ids if ids is None else ids),
+        x.q_pos0, x.live_len, x.scale)
+    res = to_host(out)
+    return (res, ws) if want_ws else res
+
+
+@pytest.mark.parametrize("select", [64, 512, 2048])
+@pytest.mark.parametrize("tail", [0, 1, 2, 3])
+def test_paged_parity_config(select, tail):
+    """4096 query rows, page-16 non-monotonic table, 4-token selection of S tokens, partial tail t."""
+    x = workloads.paged_sparse_inputs(select_tokens=select, tail=tail, seed=100 * tail + select)
+    assert_parity(_gpu(x), _oracle(x), f"S={select} t={tail}")
+
+
+def test_paged_128_entry_table():
+    """The 128-entry page-16 table geometry: 2044 rows (short last query block)."""
+    x = workloads.paged_sparse_inputs(select_tokens=512, tail=3, seed=7, nq=2044)
+    assert x.page_table.size == 128
+    assert_parity(_gpu(x), _oracle(x), "128-entry table")
+
+
+def test_paged_stale_poison():
+    """NaN in every cache slot holding no live token changes nothing and stays out of the output."""
+    x = workloads.paged_sparse_inputs(select_tokens=512, tail=2, seed=11)
+    xp = workloads.paged_sparse_inputs(select_tokens=512, tail=2, seed=11, poison_stale=True)
+    a, b = _gpu(x), _gpu(xp)
+    assert np.isfinite(b).all()
+    assert np.array_equal(a, b)
+    assert_parity(b, _oracle(x), "poisoned")
+
+
+def test_paged_identity_vs_permuted_table():
+    """The same logical cache behind the identity page table and behind a permuted one."""
+    x = workloads.paged_sparse_inputs(select_tokens=512, tail=1, seed=12)
+    ref = _oracle(x)
+    n_table = x.page_table.size
+    toks = np.arange(n_table * 16)
+    from oracle import attention as oatt
+
+    k_log = oatt.gather_paged(x.k_cache, x.page_table, 16, toks).reshape(n_table, 16, 1, 256)
+    v_log = oatt.gather_paged(x.v_cache, x.page_table, 16, toks).reshape(n_table, 16, 1, 256)
+    ident = np.arange(n_table, dtype=np.int32)
+    out_perm = _gpu(x)
+    out_id = _gpu(x, k_cache=k_log, v_cache=v_log, page_table=ident)
+    assert_parity(out_perm, ref, "permuted table")
+    assert_parity(out_id, ref, "identity table")
+
+
+def test_paged_saturated_matches_dense_causal():
+    """Selecting every block up to the diagonal reproduces dense causal attention."""
+    x = workloads.paged_sparse_inputs(select_tokens=64, tail=1, seed=13, nq=1024, saturate=True)
+    out = _gpu(x)
+    from oracle import attention as oatt
+
+    toks = np.arange(x.live_len)
+    kc = oatt.gather_paged(x.k_cache, x.page_table, 16, toks)
+    vc = oatt.gather_paged(x.v_cache, x.page_table, 16, toks)
+    ref, _ = oracle.prefill_causal(x.q, kc, vc, x.q_pos0, x.scale)
+    assert_parity(out, ref, "saturated")
+
+
+def test_paged_invalid_and_duplicate_entries_are_dropped():
+    """Out-of-range block ids, out-of-range pages and duplicates contribute nothing and are counted."""
+    import gqa_causal_flash_amd as g
+
+    x = workloads.paged_sparse_inputs(select_tokens=64, tail=1, seed=14, nq=256)
+    offs = x.qblock_offsets.astype(np.int64)
+    ids = list(x.kv_block_ids)
+    # block 0: add an id past the table; block 1: add a duplicate of its first id
+    bad_id = x.page_table.size * 4 + 5
+    new_ids = ids[:offs[1]] + [bad_id] + ids[offs[1]:offs[2]] + [ids[offs[1]]] + ids[offs[2]:]
+    new_offs = offs.copy()
+    new_offs[1:] += 1
+    new_offs[2:] += 1
+    new_ids = np.asarray(new_ids, dtype=np.int32)
+    new_offs = new_offs.astype(np.int32)
+    # a page-table entry out of range: make the table point one logical page at a missing physical page
+    pt = x.page_table.copy()
+    victim_page = 3 if ids[offs[1]] // 4 != 3 else 5
+    pt[victim_page] = 10_000
+    out, ws = _gpu(x, ids=new_ids, offs=new_offs, page_table=pt, want_ws=True)
+    dropped = g.gqa_prefill_paged_sparse_dropped(ws)
+    # reference: the same selection without the bad id and the duplicate, and without blocks of the victim page
+    counts = []
+    ref_ids = []
+    for b in range(len(offs) - 1):
+        sel = [i for i in x.kv_block_ids[offs[b]:offs[b + 1]] if i // 4 != victim_page]
+        ref_ids += sel
+        counts.append(len(sel))
+    ref_offs = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    ref = _oracle(x, ids=np.asarray(ref_ids, dtype=np.int32), offs=ref_offs)
+    n_victim = sum(1 for i in new_ids if i // 4 == victim_page)
+    assert n_victim > 0
+    assert dropped == 2 + n_victim
+    assert_parity(out, ref, "dropped entries")
+
+
+def test_paged_empty_selection_gives_zero_rows():
+    x = workloads.paged_sparse_inputs(select_tokens=64, tail=0, seed=15, nq=128)
+    offs = np.array([0, 0, x.qblock_offsets[2] - x.qblock_offsets[1]], dtype=np.int32)
+    ids = x.kv_block_ids[x.qblock_offsets[1]:x.qblock_offsets[2]]
+    out = _gpu(x, ids=ids, offs=offs)
+    assert np.array_equal(out[:64], np.zeros_like(out[:64]))
+    assert_parity(out, _oracle(x, ids=ids, offs=offs), "empty block 0")
+
+
+def test_paged_deterministic():
+    x = workloads.paged_sparse_inputs(select_tokens=2048, tail=3, seed=16)
+    assert np.array_equal(_gpu(x), _gpu(x))
