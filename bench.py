@@ -134,6 +134,86 @@ def cpu_baseline_prefill(cfg, host, seconds: float):
     )
 
 
+def paged_visible_pairs(x) -> int:
+    """Visible (query row, key) pairs of one head in a paged block-sparse workload."""
+    offs = x.qblock_offsets
+    total = 0
+    for b in range(offs.size - 1):
+        sel = np.unique(x.kv_block_ids[offs[b]:offs[b + 1]]).astype(np.int64)
+        toks = (sel[:, None] * x.kv_block_tokens + np.arange(x.kv_block_tokens)).reshape(-1)
+        toks = np.sort(toks[toks < x.live_len])
+        r0, r1 = b * x.qblock_rows, min(x.q.shape[0], (b + 1) * x.qblock_rows)
+        pos = x.q_pos0 + np.arange(r0, r1)
+        total += int(np.searchsorted(toks, pos, side="right").sum())
+    return total
+
+
+def bench_paged(select_tokens, steps, warmup, tail=1, seed=0):
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    x = workloads.paged_sparse_inputs(select_tokens=select_tokens, tail=tail, seed=seed)
+    dev = {k: torch.from_numpy(np.ascontiguousarray(getattr(x, k))).cuda()
+           for k in ("q", "k_cache", "v_cache", "page_table", "qblock_offsets", "kv_block_ids")}
+    o = torch.empty_like(dev["q"])
+    nbytes = g.gqa_prefill_paged_sparse_workspace_size(x.q.shape[0], x.kv_block_ids.size)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+
+    def step():
+        g.gqa_prefill_paged_sparse(dev["q"], dev["k_cache"], dev["v_cache"], dev["page_table"],
+                                   dev["qblock_offsets"], dev["kv_block_ids"], x.q_pos0, x.live_len, x.scale,
+                                   o=o, workspace=ws)
+
+    ms, kms = time_steps(step, steps, warmup)
+    pairs = paged_visible_pairs(x)
+    flops = 4.0 * 256 * 6 * pairs
+    # bytes the attention kernel moves: gathered K and V rows of every query block, Q and O
+    gathered = sum(max(0, int(min(x.live_len, 4 * (b + 1)) - 4 * b)) for b in x.kv_block_ids) * 2 * 512
+    moved = gathered + 2 * x.q.nbytes
+    tf = flops / (kms * 1e-3) / 1e12
+    return {
+        "workload": f"paged_sparse_q4096_page16_select{select_tokens}_tail{tail}",
+        "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "visible_pairs_per_head": pairs,
+        "roofline": {"kernel": "paged_fwd", "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 4),
+                     "moved_GBps": round(moved / (kms * 1e-3) / 1e9, 1), "traffic": None},
+        "page_ms_v100": {64: 1.010, 512: 3.204, 2048: 11.203}[select_tokens],
+    }
+
+
+def bench_verify(nq, steps, warmup, copies=3, seed=0):
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    x = workloads.verify_inputs(nq, workloads.VERIFY_CONTEXT, seed)
+    q = torch.from_numpy(x.q).cuda()
+    kvs = [(torch.from_numpy(x.k_bytes).cuda(), torch.from_numpy(x.v_bytes).cuda())]
+    for _ in range(copies - 1):  # independent copies so the 256 MiB last-level cache cannot serve them
+        kvs.append((kvs[0][0].clone(), kvs[0][1].clone()))
+    o = torch.empty_like(q)
+    nbytes = g.gqa_verify_fp8kv_workspace_size(nq, workloads.VERIFY_CONTEXT)
+    ws = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    it = [0]
+
+    def step():
+        k, v = kvs[it[0] % copies]
+        it[0] += 1
+        g.gqa_verify_fp8kv(q, k, v, x.k_scale, x.v_scale, x.scale, o=o, workspace=ws)
+
+    ms, kms = time_steps(step, steps, warmup)
+    alg = 2 * x.k_bytes.nbytes + 2 * x.q.nbytes
+    gbs = alg / (kms * 1e-3) / 1e9
+    return {
+        "workload": f"verify_fp8kv_q{nq}_ctx{workloads.VERIFY_CONTEXT}",
+        "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4), "kv_copies_rotated": copies,
+        "roofline": {"kernel": "verify_fwd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+    }
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -142,6 +222,7 @@ def main(argv=None):
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", type=int, default=workloads.HEADLINE.n_kv, help="key count of the prefill workload")
+    ap.add_argument("--no-paths", action="store_true", help="skip the paged and verifier measurements")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -187,6 +268,11 @@ def main(argv=None):
             "traffic": None,
         },
     }
+    if not args.no_paths:
+        line["paths"] = {
+            "paged_sparse": [bench_paged(sel, args.steps, args.warmup) for sel in (64, 512, 2048)],
+            "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in (2, 4, 8)],
+        }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(cfg, r["host"], args.cpu_seconds)
     print(json.dumps(line), flush=True)

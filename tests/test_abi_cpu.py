@@ -79,3 +79,68 @@ def test_prefill_rejects_before_launch(kw, status):
 def test_profile_stop_without_start_is_invalid():
     ms, n = ctypes.c_double(), ctypes.c_int32()
     assert g.lib().gqa_profile_stop(ctypes.byref(ms), ctypes.byref(n)) == g.GQA_ERR_INVALID
+
+
+def _paged(**kw):
+    a = dict(q=FAKE, kc=FAKE, vc=FAKE, pt=FAKE, n_table=257, n_pages=512, page_size=16, offs=FAKE, ids=FAKE,
+             n_ids=1000, qbr=64, kbt=4, nq=4096, q_pos0=1, live_len=4097, hq=6, hkv=1, d=256, scale=0.0625, o=FAKE,
+             ws=None, ws_bytes=0)
+    a.update(kw)
+    return g.lib().gqa_prefill_paged_sparse(a["q"], a["kc"], a["vc"], a["pt"], a["n_table"], a["n_pages"],
+                                            a["page_size"], a["offs"], a["ids"], a["n_ids"], a["qbr"], a["kbt"],
+                                            a["nq"], a["q_pos0"], a["live_len"], a["hq"], a["hkv"], a["d"],
+                                            a["scale"], a["o"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), g.GQA_ERR_INVALID),
+    (dict(pt=None), g.GQA_ERR_INVALID),
+    (dict(ids=None), g.GQA_ERR_INVALID),
+    (dict(live_len=4096), g.GQA_ERR_INVALID),       # q_pos0 + nq > live_len
+    (dict(live_len=257 * 16 + 1), g.GQA_ERR_INVALID),  # live tokens beyond the table
+    (dict(n_pages=0), g.GQA_ERR_INVALID),
+    (dict(page_size=32), g.GQA_ERR_UNSUPPORTED),
+    (dict(kbt=8), g.GQA_ERR_UNSUPPORTED),
+    (dict(qbr=128), g.GQA_ERR_UNSUPPORTED),
+    (dict(hq=8), g.GQA_ERR_UNSUPPORTED),
+    (dict(), g.GQA_ERR_WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=64), g.GQA_ERR_WORKSPACE),
+])
+def test_paged_rejects_before_launch(kw, status):
+    assert _paged(**kw) == status
+
+
+def test_paged_workspace_query():
+    n = ctypes.c_size_t()
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(4096, 1000, 64, 4, 6, 1, 256, ctypes.byref(n)) == 0
+    assert n.value >= 1000 * 8
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(0, 1000, 64, 4, 6, 1, 256, ctypes.byref(n)) == \
+        g.GQA_ERR_INVALID
+
+
+def _verify(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.01, vs=0.01, o=FAKE, nq=8, n_kv=261888, hq=6, hkv=1, d=256, scale=0.0625,
+             ws=None, ws_bytes=0)
+    a.update(kw)
+    return g.lib().gqa_verify_fp8kv(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], a["nq"], a["n_kv"], a["hq"],
+                                    a["hkv"], a["d"], a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), g.GQA_ERR_INVALID),
+    (dict(ks=0.0), g.GQA_ERR_INVALID),
+    (dict(vs=float("inf")), g.GQA_ERR_INVALID),
+    (dict(nq=0), g.GQA_ERR_INVALID),
+    (dict(nq=10, n_kv=5), g.GQA_ERR_INVALID),
+    (dict(nq=9), g.GQA_ERR_UNSUPPORTED),             # 54 packed rows > 48
+    (dict(n_kv=262145), g.GQA_ERR_UNSUPPORTED),      # past the 262144 capability
+    (dict(d=128), g.GQA_ERR_UNSUPPORTED),
+    (dict(), g.GQA_ERR_WORKSPACE),
+])
+def test_verify_rejects_before_launch(kw, status):
+    assert _verify(**kw) == status
+
+
+def test_paged_dropped_rejects_null():
+    n = ctypes.c_int32()
+    assert g.lib().gqa_prefill_paged_sparse_dropped(None, ctypes.byref(n), None) == g.GQA_ERR_INVALID
