@@ -223,6 +223,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", type=int, default=workloads.HEADLINE.n_kv, help="key count of the prefill workload")
     ap.add_argument("--no-paths", action="store_true", help="skip the paged and verifier measurements")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (3 times), as the known-size reference "
+                         "for the FETCH_SIZE / WRITE_SIZE counters")
     args = ap.parse_args(argv)
 
     if args.gpus != 1:
@@ -236,6 +239,14 @@ def main(argv=None):
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
 
+    if args.copy_calibration_mib:
+        n = args.copy_calibration_mib << 20
+        src = torch.randint(0, 255, (n,), dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(f"copy calibration: 3 x {n} bytes", file=sys.stderr)
     cfg = workloads.CausalConfig(f"causal_gqa_prefill_q8000_kv{args.kv}", nq=8000, n_kv=args.kv)
     r = bench_prefill(cfg, args.steps, args.warmup)
     value = r["flops"] / (r["ms"] * 1e-3) / 1e12

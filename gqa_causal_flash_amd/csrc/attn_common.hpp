@@ -90,9 +90,12 @@ __device__ __forceinline__ uint32_t k_lane_base(int lane) {
   const int h = lane >> 5, col = lane & 31;
   return 512u * col + 16u * (uint32_t)(h ^ (col & 15));
 }
-__device__ __forceinline__ h8 read_k_frag(const GQA_LDS char* ktile, uint32_t bk, int kb, int s) {
-  return *(const GQA_LDS h8*)(ktile + 16384 * kb + (bk ^ (32u * s)));
+// `kaddr` = LDS byte address of the tile + bk: the tile base has no bits
+// below 2^14, so it commutes with the XOR and the read costs one v_xor.
+__device__ __forceinline__ h8 read_k_frag(uint32_t kaddr, int kb, int s) {
+  return *(const GQA_LDS h8*)(uintptr_t)((kaddr ^ (32u * s)) + 16384u * kb);
 }
+__device__ __forceinline__ uint32_t lds_addr(const GQA_LDS void* p) { return (uint32_t)(uintptr_t)p; }
 
 // V^T half fragment: A operand of O^T += V^T P^T for head-dim rows
 // 32dt .. 32dt+31 and keys key0 + 4h + e (e = 0..3, key0 a multiple of 8), read

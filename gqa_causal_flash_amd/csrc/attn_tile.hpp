@@ -1,5 +1,8 @@
 // One 32-key step of the fused attention loop, shared by every kernel.
 //
+// `kaddr` is the lane's K fragment base in the staged tile (tile address +
+// k_lane_base), `vt`/`bv` the V tile and the lane's V base.
+//
 // For a wave holding C blocks of 32 packed query rows (Q as matrix-core B
 // fragments in registers, O^T accumulators, running max m and partial sum l
 // per lane) and a K/V tile staged in LDS (fp16, swizzled as described in
@@ -24,8 +27,7 @@
 namespace gqa {
 
 template <int C, class Visible>
-__device__ __forceinline__ void attend_32keys(const GQA_LDS char* kt, const GQA_LDS char* vt, uint32_t bk,
-                                              uint32_t bv, int kb, const h8 (&qf)[C][16], f16x (&acc)[C][8],
+__device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char* vt, uint32_t bv, int kb, const h8 (&qf)[C][16], f16x (&acc)[C][8],
                                               float (&m)[C], float (&l)[C], float cscale, bool mask,
                                               Visible visible) {
   const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
@@ -33,11 +35,47 @@ __device__ __forceinline__ void attend_32keys(const GQA_LDS char* kt, const GQA_
   f16x s[C];
 #pragma unroll
   for (int c = 0; c < C; ++c) s[c] = f16x{};
+  {
+    // K fragments run kPF steps ahead of the matrix cores
+    constexpr int kPF = 4;
+#ifdef GQA_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+    h8 kf[kPF];
 #pragma unroll
-  for (int si = 0; si < 16; ++si) {
-    const h8 a = read_k_frag(kt, bk, kb, si);
+    for (int j = 0; j < kPF; ++j) kf[j] = read_k_frag(kaddr, kb, j);
+#ifdef GQA_SPLITQK
+    f16x s2[C];
 #pragma unroll
-    for (int c = 0; c < C; ++c) s[c] = mfma(a, qf[c][si], s[c]);
+    for (int c = 0; c < C; ++c) s2[c] = f16x{};
+#endif
+#pragma unroll
+    for (int si = 0; si < 16; ++si) {
+      const h8 a = kf[si % kPF];
+      if (si + kPF < 16) kf[si % kPF] = read_k_frag(kaddr, kb, si + kPF);
+#pragma unroll
+      for (int c = 0; c < C; ++c) {
+#ifdef GQA_SPLITQK
+        if (si & 1) s2[c] = mfma(a, qf[c][si], s2[c]); else
+#endif
+        s[c] = mfma(a, qf[c][si], s[c]);
+      }
+    }
+#ifdef GQA_SPLITQK
+#pragma unroll
+    for (int c = 0; c < C; ++c) s[c] += s2[c];
+#endif
+    // keep that order: kPF reads up front, then one read per matrix-core step
+    __builtin_amdgcn_sched_group_barrier(0x100, kPF, 0);
+#pragma unroll
+    for (int si = 0; si < 16 - kPF; ++si) {
+      __builtin_amdgcn_sched_group_barrier(0x008, C, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, C * kPF, 0);
+#ifdef GQA_SETPRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   }
 
   h8 pk[C][2];
@@ -80,15 +118,41 @@ __device__ __forceinline__ void attend_32keys(const GQA_LDS char* kt, const GQA_
     }
   }
 
+  {
+    // V^T fragments (two transposed reads each) run kPV steps ahead
+    constexpr int kPV = 2;
+#ifdef GQA_SETPRIO
+    __builtin_amdgcn_s_setprio(1);
+#endif
+    h4 vlo[kPV], vhi[kPV];
 #pragma unroll
-  for (int dt = 0; dt < 8; ++dt) {
+    for (int j = 0; j < kPV; ++j) {
+      const int dt = j >> 1, t = j & 1;
+      vlo[j] = read_vt_half(vt, bv, 32 * kb + 16 * t, dt);
+      vhi[j] = read_vt_half(vt, bv, 32 * kb + 16 * t + 8, dt);
+    }
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int key0 = 32 * kb + 16 * t;
-      const h8 a = cat_h4(read_vt_half(vt, bv, key0, dt), read_vt_half(vt, bv, key0 + 8, dt));
+    for (int st = 0; st < 16; ++st) {
+      const int dt = st >> 1, t = st & 1;
+      const h8 a = cat_h4(vlo[st % kPV], vhi[st % kPV]);
+      if (st + kPV < 16) {
+        const int dn = (st + kPV) >> 1, tn = (st + kPV) & 1;
+        vlo[st % kPV] = read_vt_half(vt, bv, 32 * kb + 16 * tn, dn);
+        vhi[st % kPV] = read_vt_half(vt, bv, 32 * kb + 16 * tn + 8, dn);
+      }
 #pragma unroll
       for (int c = 0; c < C; ++c) acc[c][dt] = mfma(a, pk[c][t], acc[c][dt]);
     }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * kPV, 0);
+#pragma unroll
+    for (int st = 0; st < 16 - kPV; ++st) {
+      __builtin_amdgcn_sched_group_barrier(0x008, C, 0);
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, C * kPV, 0);
+#ifdef GQA_SETPRIO
+    __builtin_amdgcn_s_setprio(0);
+#endif
   }
 }
 

@@ -267,7 +267,7 @@ __global__ __launch_bounds__(256, 1) void paged_fwd(PagedParams p) {
         kp[4 * j + 2] = x.z;
         kp[4 * j + 3] = x.w;
       }
-      attend_32keys<1>(kt, vt, bk, bv, kb, qf, acc, m, l, p.c, true, [&](int, int vv) { return kp[vv] <= pos; });
+      attend_32keys<1>(lds_addr(kt) + bk, vt, bv, kb, qf, acc, m, l, p.c, true, [&](int, int vv) { return kp[vv] <= pos; });
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();

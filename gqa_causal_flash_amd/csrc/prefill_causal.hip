@@ -46,6 +46,7 @@ struct PrefillParams {
   int q_pos0;
   int nqb;
   int grid;
+  int split;  // key-split pieces per q-block (0: stream-K split)
   uint32_t part_bytes;
   float c;  // scale * log2(e): scores are kept in log2 units
 };
@@ -160,7 +161,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
       // next to their use, instead of being hoisted and held in registers
       asm volatile("" : "+v"(bk), "+v"(bv));
       // mask only blocks that cross the causal diagonal of some row of the wave
-      attend_32keys<C>(kt, vt, bk, bv, kb, qf, acc, m, l, p.c, k0 + 31 > wpos_lo,
+      attend_32keys<C>(lds_addr(kt) + bk, vt, bv, kb, qf, acc, m, l, p.c, k0 + 31 > wpos_lo,
                        [&](int c, int vv) { return k0 + lane_key(vv, half) <= pos[c]; });
     }
     wait_vmem();
@@ -193,6 +194,14 @@ template <int C, int W>
 __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
   const int w = blockIdx.x;
+  if (p.split > 0) {
+    const int b = w / p.split, j = w % p.split;
+    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+    const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
+    // the split never exceeds the shortest q-block's tile count, so lo < hi
+    prefill_piece<C, W>(p, smem, b, lo, hi, p.split == 1, w);
+    return;
+  }
   long long t0 = prefill_range_start(w, p.total, p.grid);
   const long long t1 = prefill_range_start(w + 1, p.total, p.grid);
   if (t0 >= t1) return;
@@ -221,11 +230,19 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p)
 __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   const int b = blockIdx.x >> 2;
   const int quarter = blockIdx.x & 3;
-  long long cb = 0;
-  for (int i = 0; i < b; ++i) cb += prefill_block_tiles(i, p.nrows, p.q_pos0);
-  const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
-  const int w0 = prefill_owner(cb, p.total, p.grid);
-  const int w1 = prefill_owner(cb + nt - 1, p.total, p.grid);
+  int w0, w1, slot0;
+  if (p.split > 0) {  // pieces of q-block b are slots b*split .. b*split + split - 1
+    w0 = 0;
+    w1 = p.split - 1;
+    slot0 = b * p.split;
+  } else {
+    long long cb = 0;
+    for (int i = 0; i < b; ++i) cb += prefill_block_tiles(i, p.nrows, p.q_pos0);
+    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+    w0 = prefill_owner(cb, p.total, p.grid);
+    w1 = prefill_owner(cb + nt - 1, p.total, p.grid);
+    slot0 = b;
+  }
   if (w0 == w1) return;  // done whole by one workgroup, already written
   const int tid = threadIdx.x;
   const int rl = quarter * 64 + (tid & 63);
@@ -233,7 +250,7 @@ __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
   float M = -INFINITY;
   for (int w = w0; w <= w1; ++w) {
-    const uint32_t sb = (uint32_t)(w + b) * (uint32_t)(kPartialFloats * 4);
+    const uint32_t sb = (uint32_t)(w + slot0) * (uint32_t)(kPartialFloats * 4);
     M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0)));
   }
   f4 o[16];
@@ -241,7 +258,7 @@ __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   for (int j = 0; j < 16; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   for (int w = w0; w <= w1; ++w) {
-    const uint32_t sb = (uint32_t)(w + b) * (uint32_t)(kPartialFloats * 4);
+    const uint32_t sb = (uint32_t)(w + slot0) * (uint32_t)(kPartialFloats * 4);
     const float mw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
     const float lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
     const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
@@ -282,6 +299,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.q_pos0 = q_pos0;
   p.nqb = s.nqb;
   p.grid = s.grid;
+  p.split = s.split;
   p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
   p.c = scale * kLog2e;
   prof_before(stream);

@@ -34,6 +34,7 @@ struct PrefillSched {
   int nqb;          // number of q-blocks
   long long total;  // T
   int grid;         // G
+  int split;        // >0: key-split mode with this many pieces per q-block (see below)
 };
 
 __host__ __device__ inline int prefill_block_tiles(int b, int nrows, int q_pos0) {
@@ -53,6 +54,17 @@ __host__ __device__ inline int prefill_owner(long long x, long long total, int g
   return (int)(((x + 1) * grid - 1) / total);
 }
 
+// Key-split mode (used when split > 0): q-block b's tiles are cut into `split`
+// equal key ranges, piece j = tiles floor(j n_b / split) .. floor((j+1) n_b /
+// split) - 1, and workgroup u = b * split + j runs piece j of q-block b.  With
+// split dividing 8, the round-robin placement of workgroup u on XCD u % 8 puts
+// only piece u % split on each XCD, so the 32 workgroups of an XCD stream the
+// same K/V range at the same pace and share that XCD's L2.  Piece j of q-block
+// b leaves its partial in slot u.
+#ifndef GQA_PREFILL_KEYSPLIT
+#define GQA_PREFILL_KEYSPLIT 1
+#endif
+
 inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
   PrefillSched s;
   s.nrows = nq * hq;
@@ -66,6 +78,20 @@ inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
   if (g > kTargetGrid) g = kTargetGrid;
   if (g > t) g = t;
   s.grid = (int)g;
+  s.split = 0;
+  if (GQA_PREFILL_KEYSPLIT) {
+    // smallest power-of-two split (<= 8) giving at least two workgroups per compute unit,
+    // never more pieces than the shortest q-block has tiles
+    int minnt = 1 << 30;
+    for (int b = 0; b < s.nqb; ++b) {
+      const int nt = prefill_block_tiles(b, s.nrows, q_pos0);
+      if (nt < minnt) minnt = nt;
+    }
+    int sp = 1;
+    while (sp < 8 && (long long)s.nqb * sp < 2LL * kTargetGrid && sp * 2 <= minnt) sp *= 2;
+    s.split = sp;
+    s.grid = s.nqb * sp;
+  }
   return s;
 }
 
@@ -74,6 +100,7 @@ constexpr size_t kPartialFloats = (size_t)256 * 256 + 256 + 256;
 
 // True when some q-block is cut between workgroups (its partials need merging).
 inline bool prefill_needs_merge(const PrefillSched& s) {
+  if (s.split > 0) return s.split > 1;
   long long cb = 0;
   for (int b = 0; b < s.nqb; ++b) {
     const int nt = prefill_block_tiles(b, s.nrows, s.q_pos0);
@@ -85,6 +112,7 @@ inline bool prefill_needs_merge(const PrefillSched& s) {
 
 inline size_t prefill_workspace_bytes(const PrefillSched& s) {
   if (!prefill_needs_merge(s)) return 0;
+  if (s.split > 0) return (size_t)s.grid * kPartialFloats * sizeof(float);
   return (size_t)(s.grid + s.nqb) * kPartialFloats * sizeof(float);
 }
 

@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256, 1) void verify_fwd(VerifyParams p) {
     if (live && rows_active) {
       const int k0 = t * kVTileKeys;
       asm volatile("" : "+v"(bk), "+v"(bv));
-      attend_32keys<1>(kt, vt, bk, bv, 0, qf, acc, m, l, p.c, k0 + 31 > pos_min,
+      attend_32keys<1>(lds_addr(kt) + bk, vt, bv, 0, qf, acc, m, l, p.c, k0 + 31 > pos_min,
                        [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; });
     }
   }
