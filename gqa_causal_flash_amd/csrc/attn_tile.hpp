@@ -26,45 +26,27 @@
 
 namespace gqa {
 
-template <int C, class Visible>
-__device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char* vt, uint32_t bv, int kb, const h8 (&qf)[C][16], f16x (&acc)[C][8],
-                                              float (&m)[C], float (&l)[C], float cscale, bool mask,
-                                              Visible visible) {
-  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
-
-  f16x s[C];
+// S^T[32 keys][32C rows] = K Q^T for keys 32kb .. 32kb+31 of the staged tile.
+template <int C>
+__device__ __forceinline__ void qk_32keys(uint32_t kaddr, int kb, const h8 (&qf)[C][16], f16x (&s)[C]) {
 #pragma unroll
   for (int c = 0; c < C; ++c) s[c] = f16x{};
   {
     // K fragments run kPF steps ahead of the matrix cores
-    constexpr int kPF = 4;
-#ifdef GQA_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
+#ifndef GQA_KPF
+#define GQA_KPF 4
 #endif
+    constexpr int kPF = GQA_KPF;
     h8 kf[kPF];
 #pragma unroll
     for (int j = 0; j < kPF; ++j) kf[j] = read_k_frag(kaddr, kb, j);
-#ifdef GQA_SPLITQK
-    f16x s2[C];
-#pragma unroll
-    for (int c = 0; c < C; ++c) s2[c] = f16x{};
-#endif
 #pragma unroll
     for (int si = 0; si < 16; ++si) {
       const h8 a = kf[si % kPF];
       if (si + kPF < 16) kf[si % kPF] = read_k_frag(kaddr, kb, si + kPF);
 #pragma unroll
-      for (int c = 0; c < C; ++c) {
-#ifdef GQA_SPLITQK
-        if (si & 1) s2[c] = mfma(a, qf[c][si], s2[c]); else
-#endif
-        s[c] = mfma(a, qf[c][si], s[c]);
-      }
+      for (int c = 0; c < C; ++c) s[c] = mfma(a, qf[c][si], s[c]);
     }
-#ifdef GQA_SPLITQK
-#pragma unroll
-    for (int c = 0; c < C; ++c) s[c] += s2[c];
-#endif
     // keep that order: kPF reads up front, then one read per matrix-core step
     __builtin_amdgcn_sched_group_barrier(0x100, kPF, 0);
 #pragma unroll
@@ -73,12 +55,14 @@ __device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, C * kPF, 0);
-#ifdef GQA_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   }
+}
 
-  h8 pk[C][2];
+// Online-softmax update from the scores of 32 keys; returns P^T as fp16 B operands.
+template <int C, class Visible>
+__device__ __forceinline__ void softmax_32keys(f16x (&s)[C], f16x (&acc)[C][8], float (&m)[C], float (&l)[C],
+                                               float cscale, bool mask, Visible visible, h8 (&pk)[C][2]) {
+  const h2 ones = {(_Float16)1.0f, (_Float16)1.0f};
 #pragma unroll
   for (int c = 0; c < C; ++c) {
     if (mask) {
@@ -118,12 +102,19 @@ __device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char
     }
   }
 
+}
+
+// O^T[256 d][32C rows] += V^T[256 d][32 keys] P^T for keys 32kb .. 32kb+31 of the staged tile.
+template <int C>
+__device__ __forceinline__ void pv_32keys(const GQA_LDS char* vt, uint32_t bv, int kb, const h8 (&pk)[C][2],
+                                          f16x (&acc)[C][8]) {
   {
-    // V^T fragments (two transposed reads each) run kPV steps ahead
-    constexpr int kPV = 2;
-#ifdef GQA_SETPRIO
-    __builtin_amdgcn_s_setprio(1);
+    // V^T fragments (two transposed reads each) run kPV steps ahead; step st
+    // is head-dim tile st / 2 and key half st % 2.
+#ifndef GQA_KPV
+#define GQA_KPV 2
 #endif
+    constexpr int kPV = GQA_KPV;
     h4 vlo[kPV], vhi[kPV];
 #pragma unroll
     for (int j = 0; j < kPV; ++j) {
@@ -150,10 +141,18 @@ __device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char
       __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
     }
     __builtin_amdgcn_sched_group_barrier(0x008, C * kPV, 0);
-#ifdef GQA_SETPRIO
-    __builtin_amdgcn_s_setprio(0);
-#endif
   }
+}
+
+template <int C, class Visible>
+__device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char* vt, uint32_t bv, int kb,
+                                              const h8 (&qf)[C][16], f16x (&acc)[C][8], float (&m)[C],
+                                              float (&l)[C], float cscale, bool mask, Visible visible) {
+  f16x s[C];
+  qk_32keys<C>(kaddr, kb, qf, s);
+  h8 pk[C][2];
+  softmax_32keys<C>(s, acc, m, l, cscale, mask, visible, pk);
+  pv_32keys<C>(vt, bv, kb, pk, acc);
 }
 
 // Key index inside the 32-key block held by this lane's accumulator register vv.

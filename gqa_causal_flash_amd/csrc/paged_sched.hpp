@@ -28,8 +28,22 @@ constexpr int kPagedWGsPerQBlock = kQBlockRows / kPagedRowsPerWG;  // 3
 constexpr int kPagedMagic = 0x47514150;  // "PAQG"
 constexpr int kSortMax = 2048;           // selections up to this many blocks are sorted
 
+// The attention kernel cuts each query block's selection into `pieces` equal
+// runs of 32-key sub-tiles (more pieces for longer selections, so that the
+// whole chip is busy); with more than one piece every (row group, piece)
+// leaves a partial of 128 rows that a merge kernel combines.
+inline int paged_pieces(int nqb, int n_ids) {
+  const long long avg_blocks = nqb > 0 ? (long long)n_ids / nqb : 0;
+  if (avg_blocks <= 32) return 1;
+  if (avg_blocks <= 128) return 2;
+  return 4;
+}
+
+constexpr size_t kPagedSlotFloats = (size_t)kPagedRowsPerWG * 256 + 2 * kPagedRowsPerWG;
+
 struct PagedLayout {
-  size_t err, beg, cnt, entries, total;
+  size_t err, beg, cnt, entries, part, total;
+  int pieces;
 };
 
 inline PagedLayout paged_layout(int nqb, int n_ids) {
@@ -38,7 +52,10 @@ inline PagedLayout paged_layout(int nqb, int n_ids) {
   L.beg = L.err + 4 * (size_t)nqb;
   L.cnt = L.beg + 4 * (size_t)nqb;
   L.entries = (L.cnt + 4 * (size_t)nqb + 15) / 16 * 16;
-  L.total = L.entries + 8 * (size_t)(n_ids > 0 ? n_ids : 1);
+  L.part = (L.entries + 8 * (size_t)(n_ids > 0 ? n_ids : 1) + 255) / 256 * 256;
+  L.pieces = paged_pieces(nqb, n_ids);
+  const size_t slots = L.pieces > 1 ? (size_t)nqb * kPagedWGsPerQBlock * L.pieces : 0;
+  L.total = L.part + slots * kPagedSlotFloats * 4;
   return L;
 }
 

@@ -36,7 +36,6 @@ namespace gqa {
 
 namespace {
 
-constexpr int kTileBytes = 64 * kRowBytes;  // 32 KiB
 constexpr int kWaves = 4;
 constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // buffer offset past any cache: reads zeros
 
@@ -50,7 +49,9 @@ struct PagedParams {
   _Float16* o;
   char* ws;
   int n_table, n_pages, n_ids, nq, nrows, nqb, q_pos0, live_len;
-  size_t off_err, off_beg, off_cnt, off_entries;
+  size_t off_err, off_beg, off_cnt, off_entries, off_part;
+  uint32_t part_bytes;
+  int pieces;
   float c;
 };
 
@@ -169,41 +170,60 @@ __global__ __launch_bounds__(256) void paged_prepass(PagedParams p) {
 }
 
 // ------------------------------------------------------------------ attention
-// Wave w stages rows 16w .. 16w+15 of the 64-key tile (entries 4w .. 4w+3 of
-// the tile); copy i covers rows 16w+2i, 16w+2i+1 = tokens 2(i%2), 2(i%2)+1 of
-// entry 4w + i/2.  Lanes 0..15 also record the logical position of row 16w+l.
-__device__ __forceinline__ void paged_issue_tile(const PagedParams& p, rsrc_t rk, rsrc_t rv, const int2* ent,
-                                                 int e0, int e_end, char* kdst, char* vdst, int* kpos, int wave,
-                                                 int lane, uint32_t kl, uint32_t vl) {
+constexpr int kSubKeys = 32;                     // keys per sub-tile = 8 blocks
+constexpr int kSubBytes = kSubKeys * kRowBytes;  // 16 KiB for K or V
+
+// Wave w stages rows 8w .. 8w+7 of a 32-key sub-tile, i.e. entries 2w, 2w+1
+// of the sub-tile; copy i covers rows 8w+2i, 8w+2i+1 = tokens 2(i%2), 2(i%2)+1
+// of entry 2w + i/2.  The swizzle index of row 8w+2i+h is x = 2j + h with
+// j = 4(w%2) + i, which gives the lane offsets kl ^ 32j (K) and
+// vl ^ 128(j%4) (V) used by the dense kernel, shifted to the entry's
+// physical row.  Lanes 0..7 also record the logical position of row 8w+l.
+__device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk, rsrc_t rv, const int2* ent,
+                                                int e0, int e_end, char* kdst, char* vdst, int* kpos, int wave,
+                                                int lane, uint32_t kl, uint32_t vl) {
   const int half = lane >> 5;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int e = e0 + 4 * wave + i / 2;  // wave-uniform
-    int2 en = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
+  for (int i = 0; i < 4; ++i) {
+    const int e = e0 + 2 * wave + i / 2;  // wave-uniform
+    const int2 en = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
     const int u = 2 * (i & 1) + half;
     const bool live = en.x >= 0 && en.y + u < p.live_len;
-    // x = row % 16 = 2i + half (wave base 16w is a multiple of 16): swizzles as in the dense kernel
+    const uint32_t j = (uint32_t)(4 * (wave & 1) + i);
     const uint32_t base = (uint32_t)(en.x + u) * kRowBytes - (uint32_t)(2 * i + half) * kRowBytes;
-    const uint32_t vk = live ? base + (kl ^ (32u * i)) + 1024u * i : kNoRow;
-    const uint32_t vv = live ? base + (vl ^ (128u * (i & 3))) + 1024u * i : kNoRow;
-    const int r0 = 16 * wave + 2 * i;
+    const uint32_t vk = live ? base + (kl ^ (32u * j)) + 1024u * i : kNoRow;
+    const uint32_t vv = live ? base + (vl ^ (128u * (j & 3))) + 1024u * i : kNoRow;
+    const int r0 = 8 * wave + 2 * i;
     load_lds_16B(rk, (GQA_LDS char*)(kdst + r0 * kRowBytes), vk, 0);
     load_lds_16B(rv, (GQA_LDS char*)(vdst + r0 * kRowBytes), vv, 0);
   }
-  if (lane < 16) {
-    const int e = e0 + 4 * wave + lane / 4;
+  if (lane < 8) {
+    const int e = e0 + 2 * wave + lane / 4;
     const int2 en = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
     const int u = lane & 3;
     const bool live = en.x >= 0 && en.y + u < p.live_len;
-    kpos[16 * wave + lane] = live ? en.y + u : 0x7FFFFFFF;
+    kpos[8 * wave + lane] = live ? en.y + u : 0x7FFFFFFF;
   }
 }
 
-__global__ __launch_bounds__(256, 1) void paged_fwd(PagedParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
-  __shared__ __attribute__((aligned(16))) int kpos_s[2][64];
-  const int b = blockIdx.x / kPagedWGsPerQBlock;
-  const int g = blockIdx.x % kPagedWGsPerQBlock;
+// Workgroup id -> (query block, row group, piece).  Ids u with the same u % 8
+// run on the same XCD, so every workgroup of one query block is given the same
+// u % 8 and its gathered K/V rows are shared through that XCD's L2.
+__device__ __forceinline__ bool paged_unit(int u, int nqb, int pieces, int& b, int& g, int& j) {
+  const int per_block = kPagedWGsPerQBlock * pieces;
+  const int x = u & 7, rest = u >> 3;
+  b = (rest / per_block) * 8 + x;
+  const int within = rest % per_block;
+  g = within / pieces;
+  j = within % pieces;
+  return b < nqb;
+}
+
+__global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kSubBytes];  // V 0/16 KiB, K 32/48 KiB
+  __shared__ __attribute__((aligned(16))) int kpos_s[2][kSubKeys];
+  int b, g, pj;
+  if (!paged_unit(blockIdx.x, p.nqb, p.pieces, b, g, pj)) return;
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -218,14 +238,17 @@ __global__ __launch_bounds__(256, 1) void paged_fwd(PagedParams p) {
   const int n = cntp[b];
   const int e_beg = begp[b];
   const int e_end = e_beg + n;
-  const int ntiles = (n + 15) / 16;
+  const int n_sub = (n + 7) / 8;
+  const int s_lo = (int)((long long)pj * n_sub / p.pieces);
+  const int s_hi = (int)((long long)(pj + 1) * n_sub / p.pieces);
 
   const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
   const uint32_t cache_bytes = (uint32_t)p.n_pages * kPageSize * kRowBytes;
   const rsrc_t rk = make_rsrc(p.kc, cache_bytes);
   const rsrc_t rv = make_rsrc(p.vc, cache_bytes);
 
-  const int row = b * kQBlockRows + g * kPagedRowsPerWG + 32 * wave + col;
+  const int row_local = 32 * wave + col;  // row inside the 128-row group
+  const int row = b * kQBlockRows + g * kPagedRowsPerWG + row_local;
   const int pos = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
   h8 qf[1][16];
   {
@@ -240,49 +263,94 @@ __global__ __launch_bounds__(256, 1) void paged_fwd(PagedParams p) {
   uint32_t bk = k_lane_base(lane);
   uint32_t bv = v_lane_base(lane);
 
-  if (ntiles > 0) {
-    paged_issue_tile(p, rk, rv, ent, e_beg, e_end, smem + 2 * kTileBytes, smem, kpos_s[0], wave, lane, kl, vl);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  auto step = [&](auto bufc, int t) {
-    constexpr int BUF = decltype(bufc)::value;
-    if (t + 1 < ntiles)
-      paged_issue_tile(p, rk, rv, ent, e_beg + 16 * (t + 1), e_end, smem + (2 + (BUF ^ 1)) * kTileBytes,
-                       smem + (BUF ^ 1) * kTileBytes, kpos_s[BUF ^ 1], wave, lane, kl, vl);
-    const GQA_LDS char* kt = (const GQA_LDS char*)smem + (2 + BUF) * kTileBytes;
-    const GQA_LDS char* vt = (const GQA_LDS char*)smem + BUF * kTileBytes;
-    const int keys_here = min(64, 4 * (n - 16 * t));
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      if (32 * kb >= keys_here) continue;
-      asm volatile("" : "+v"(bk), "+v"(bv));
-      // logical positions of this lane's 16 keys: runs of 4 at 32kb + 8j + 4*half
-      int kp[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int4 x = *(const int4*)&kpos_s[BUF][32 * kb + 8 * j + 4 * half];
-        kp[4 * j] = x.x;
-        kp[4 * j + 1] = x.y;
-        kp[4 * j + 2] = x.z;
-        kp[4 * j + 3] = x.w;
-      }
-      attend_32keys<1>(lds_addr(kt) + bk, vt, bv, kb, qf, acc, m, l, p.c, true, [&](int, int vv) { return kp[vv] <= pos; });
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+  auto issue = [&](int x) {
+    const int buf = x & 1;
+    paged_issue_sub(p, rk, rv, ent, e_beg + 8 * x, e_end, smem + (2 + buf) * kSubBytes, smem + buf * kSubBytes,
+                    kpos_s[buf], wave, lane, kl, vl);
   };
-  for (int t = 0; t < ntiles; t += 2) {
-    step(std::integral_constant<int, 0>{}, t);
-    if (t + 1 < ntiles) step(std::integral_constant<int, 1>{}, t + 1);
+  if (s_lo < s_hi) issue(s_lo);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  for (int x = s_lo; x < s_hi; ++x) {
+    const int buf = (x - s_lo) & 1;
+    if (x + 1 < s_hi) issue(x + 1);  // lands in the other slot
+    asm volatile("" : "+v"(bk), "+v"(bv));
+    int kp[16];
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const int4 v4 = *(const int4*)&kpos_s[(x & 1)][8 * q4 + 4 * half];
+      kp[4 * q4] = v4.x;
+      kp[4 * q4 + 1] = v4.y;
+      kp[4 * q4 + 2] = v4.z;
+      kp[4 * q4 + 3] = v4.w;
+    }
+    (void)buf;
+    attend_32keys<1>(lds_addr((const GQA_LDS char*)smem + (2 + (x & 1)) * kSubBytes) + bk,
+                     (const GQA_LDS char*)smem + (x & 1) * kSubBytes, bv, 0, qf, acc, m, l, p.c, true,
+                     [&](int, int vv) { return kp[vv] <= pos; });
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
   }
 
   const float lt = swap_halves_sum(l[0]);
-  // rows of this workgroup that belong to the next query block (a short last
-  // block) or lie past the end are not written
-  const int row_end = min(p.nrows, (b + 1) * kQBlockRows);
-  const rsrc_t ro = make_rsrc(p.o, (uint32_t)row_end * kRowBytes);
-  store_rows_f16(ro, row, half, acc[0], lt, 1.0f);
+  if (p.pieces == 1) {
+    // rows of a short last query block that fall past the end are not written
+    const int row_end = min(p.nrows, (b + 1) * kQBlockRows);
+    const rsrc_t ro = make_rsrc(p.o, (uint32_t)row_end * kRowBytes);
+    store_rows_f16(ro, row, half, acc[0], lt, 1.0f);
+  } else {
+    const rsrc_t rp = make_rsrc(p.ws + p.off_part, p.part_bytes);
+    const int slot = ((b * kPagedWGsPerQBlock) + g) * p.pieces + pj;
+    store_partial(rp, (uint32_t)slot * (uint32_t)(kPagedSlotFloats * 4), kPagedRowsPerWG, row_local, half, acc[0],
+                  m[0], lt);
+  }
+}
+
+// Merge of the pieces of each 128-row group: workgroup (group, half) takes 64
+// rows; thread (row, 64 columns).
+__global__ __launch_bounds__(256) void paged_merge(PagedParams p) {
+  const int group = blockIdx.x >> 1;  // = b * 3 + g
+  const int rl = (blockIdx.x & 1) * 64 + (threadIdx.x & 63);
+  const int dq = threadIdx.x >> 6;
+  const int row = group * kPagedRowsPerWG + rl;
+  const int b = group / kPagedWGsPerQBlock;
+  if (row >= min(p.nrows, (b + 1) * kQBlockRows)) return;
+  const rsrc_t rp = make_rsrc(p.ws + p.off_part, p.part_bytes);
+  const uint32_t slot_bytes = (uint32_t)(kPagedSlotFloats * 4);
+  const uint32_t m_off = (uint32_t)(kPagedRowsPerWG * kHeadDim * 4);
+  float M = -INFINITY;
+  for (int j = 0; j < p.pieces; ++j) {
+    const uint32_t sb = (uint32_t)(group * p.pieces + j) * slot_bytes;
+    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0)));
+  }
+  f4 o[16];
+#pragma unroll
+  for (int q = 0; q < 16; ++q) o[q] = f4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int j = 0; j < p.pieces; ++j) {
+    const uint32_t sb = (uint32_t)(group * p.pieces + j) * slot_bytes;
+    const float mj = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0));
+    const float lj =
+        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kPagedRowsPerWG + rl) * 4, 0, 0));
+    const float a = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
+    L += a * lj;
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const u4 x =
+          __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((16 * dq + q) * kPagedRowsPerWG + rl) * 16), 0, 0);
+      o[q] += a * __builtin_bit_cast(f4, x);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+  const uint32_t obase = (uint32_t)row * kRowBytes + 128 * dq;
+#pragma unroll
+  for (int q = 0; q < 16; q += 2) {
+    const h2 a0 = cvt2(o[q][0] * inv, o[q][1] * inv), a1 = cvt2(o[q][2] * inv, o[q][3] * inv);
+    const h2 b0 = cvt2(o[q + 1][0] * inv, o[q + 1][1] * inv), b1 = cvt2(o[q + 1][2] * inv, o[q + 1][3] * inv);
+    const h8 v = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    store_16B(ro, obase + q * 8, __builtin_bit_cast(u4, v));
+  }
 }
 
 }  // namespace
@@ -313,15 +381,22 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   p.off_beg = L.beg;
   p.off_cnt = L.cnt;
   p.off_entries = L.entries;
+  p.off_part = L.part;
+  p.part_bytes = (uint32_t)(L.total - L.part);
+  p.pieces = L.pieces;
   p.c = scale * kLog2e;
   hipLaunchKernelGGL(paged_prepass, dim3(p.nqb), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  // ids are grouped by XCD (see paged_unit): round the query blocks up to a multiple of 8
+  const int units = ((p.nqb + 7) / 8) * 8 * kPagedWGsPerQBlock * p.pieces;
   prof_before(stream);
-  hipLaunchKernelGGL(paged_fwd, dim3(p.nqb * kPagedWGsPerQBlock), dim3(64 * kWaves), 0, stream, p);
+  hipLaunchKernelGGL(paged_fwd, dim3(units), dim3(64 * kWaves), 0, stream, p);
   e = hipGetLastError();
   prof_after(stream);
-  return e;
+  if (e != hipSuccess || p.pieces == 1) return e;
+  hipLaunchKernelGGL(paged_merge, dim3(p.nqb * kPagedWGsPerQBlock * 2), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

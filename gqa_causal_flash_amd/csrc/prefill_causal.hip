@@ -32,7 +32,7 @@ constexpr int kTileBytes = kTileKeys * kRowBytes;  // 32 KiB per K or V tile
 #define GQA_PREFILL_C 1
 #endif
 constexpr int kPrefillC = GQA_PREFILL_C;
-constexpr int kPrefillW = 8 / kPrefillC;
+constexpr int kPrefillW = kRowsPerBlock / (32 * kPrefillC);
 
 struct PrefillParams {
   const _Float16* q;
@@ -65,12 +65,13 @@ __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" 
 // needs), the byte offset from the wave's first row is
 // 2i*512 + l/32*512 + 16*(l%32 ^ swz(r)): for K, swz(r) = r % 16 gives
 // (kl ^ 32(i + 4*(w%2 when W=8))) + 1024i ... computed below per copy.
-template <int W>
-__device__ __forceinline__ void issue_tile(rsrc_t rk, rsrc_t rv, int tile, char* kdst, char* vdst, int wave,
-                                           uint32_t kl, uint32_t vl) {
-  constexpr int kRowsPerWave = kTileKeys / W;
+template <int W, int TK = kTileKeys>
+__device__ __forceinline__ void issue_rows(rsrc_t rk, rsrc_t rv, uint32_t tile_byte, char* kdst, char* vdst,
+                                           int wave, uint32_t kl, uint32_t vl) {
+  constexpr int kRowsPerWave = TK / W;
   constexpr int kCopies = kRowsPerWave / 2;
-  const uint32_t soff = (uint32_t)tile * (kTileKeys * kRowBytes) + (uint32_t)wave * (kRowsPerWave * kRowBytes);
+  static_assert(kCopies >= 1 && kRowsPerWave <= 16, "2..16 rows per wave");
+  const uint32_t soff = tile_byte + (uint32_t)wave * (kRowsPerWave * kRowBytes);
   // copy i covers rows r0 = kRowsPerWave*wave + 2i (+1); its index within the
   // 16-row swizzle period is j = (r0 % 16) / 2
   const int jbase = (kRowsPerWave * wave % 16) / 2;
@@ -81,6 +82,12 @@ __device__ __forceinline__ void issue_tile(rsrc_t rk, rsrc_t rv, int tile, char*
     load_lds_16B(rk, (GQA_LDS char*)(kdst + r0 * kRowBytes), kl ^ (32u * j), soff + 1024u * i);
     load_lds_16B(rv, (GQA_LDS char*)(vdst + r0 * kRowBytes), vl ^ (128u * (j & 3)), soff + 1024u * i);
   }
+}
+
+template <int W>
+__device__ __forceinline__ void issue_tile(rsrc_t rk, rsrc_t rv, int tile, char* kdst, char* vdst, int wave,
+                                           uint32_t kl, uint32_t vl) {
+  issue_rows<W>(rk, rv, (uint32_t)tile * (kTileKeys * kRowBytes), kdst, vdst, wave, kl, vl);
 }
 
 // Partial slot layout (fp32): acc[64 column quads][256 rows][4], m[256], l[256].
@@ -190,16 +197,218 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
   }
 }
 
+// Phase-shifted variant of prefill_piece for 8 waves of 32 rows.  Keys are
+// handled in 32-key sub-tiles held in a 4-deep LDS ring (V sub-tiles at 0, 16,
+// 32, 48 KiB; K at 64 .. 112 KiB).  In phase ph, waves 0-3 run
+// scores/softmax/PV of sub-tile ph, while waves 4-7 (one per SIMD as well)
+// run softmax/PV of sub-tile ph-1 and then the scores of sub-tile ph.  The two
+// waves of a SIMD are therefore in different parts of the step at any time:
+// the softmax arithmetic of one overlaps the matrix-core work of the other.
+// Sub-tile ph+2 is loaded during phase ph (into the slot sub-tile ph-2 used),
+// and each wave's loads of sub-tile ph+1 are complete before the barrier that
+// ends phase ph.
+__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
+
+__device__ __forceinline__ void prefill_piece_pingpong(const PrefillParams& p, char* smem, int b, int tile_lo,
+                                                       int tile_hi, bool full, int slot) {
+  constexpr int W = 8;
+  constexpr int kSub = 32;
+  constexpr int kSubBytes = kSub * kRowBytes;  // 16 KiB per K or V sub-tile
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int trail = wave >> 2;  // 0: waves 0-3, 1: waves 4-7
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const uint32_t kl = 512u * half + 16u * (uint32_t)(col ^ half);
+  const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
+
+  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
+  const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes);
+  const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes);
+
+  const int row_base = b * kRowsPerBlock + wave * 32;
+  const bool wave_active = row_base < p.nrows;
+  const int wrow_hi = min(row_base + 31, p.nrows - 1);
+  const int wpos_lo = p.q_pos0 + row_base / kGroup;
+  const int wpos_hi = p.q_pos0 + wrow_hi / kGroup;
+
+  int pos[1];
+  h8 qf[1][16];
+  {
+    const int row = row_base + col;
+    pos[0] = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
+    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
+  }
+  f16x acc[1][8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
+  float m[1] = {-INFINITY}, l[1] = {0.f};
+  uint32_t bk = k_lane_base(lane);
+  uint32_t bv = v_lane_base(lane);
+
+  const int n_sub = 2 * (tile_hi - tile_lo);
+  const int key_base = tile_lo * kTileKeys;
+  auto issue_sub = [&](int x) {
+    const int buf = x & 3;
+    issue_rows<W, kSub>(rk, rv, (uint32_t)(key_base + kSub * x) * kRowBytes, smem + (4 + buf) * kSubBytes,
+                        smem + buf * kSubBytes, wave, kl, vl);
+  };
+  auto visible_at = [&](int k0) { return [=](int c, int vv) { return k0 + lane_key(vv, half) <= pos[c]; }; };
+
+  if (n_sub > 0) issue_sub(0);
+  if (n_sub > 1) issue_sub(1);
+  wait_vmem();
+  __syncthreads();
+
+  // One code path for both groups: leaders compute the scores of sub-tile ph
+  // first, trailers last (carrying them into the next phase).
+  f16x sc[1];
+  int x = -1;  // sub-tile whose scores are in sc, -1 if none
+  auto scores = [&](int ph) {
+    const int k0 = key_base + kSub * ph;
+    if (ph < n_sub && wave_active && k0 <= wpos_hi) {
+      qk_32keys<1>(lds_addr((const GQA_LDS char*)smem + (4 + (ph & 3)) * kSubBytes) + bk, 0, qf, sc);
+      x = ph;
+    }
+  };
+  for (int ph = 0; ph <= n_sub; ++ph) {
+    const bool load = ph + 2 < n_sub;
+    if (load) issue_sub(ph + 2);
+    asm volatile("" : "+v"(bk), "+v"(bv));
+    if (trail == 0) scores(ph);
+    if (x >= 0) {
+      const int k0 = key_base + kSub * x;
+      h8 pk[1][2];
+      softmax_32keys<1>(sc, acc, m, l, p.c, k0 + 31 > wpos_lo, visible_at(k0), pk);
+      pv_32keys<1>((const GQA_LDS char*)smem + (x & 3) * kSubBytes, bv, 0, pk, acc);
+      x = -1;
+    }
+    if (trail == 1) scores(ph);
+    if (load)
+      wait_vmem_4();  // this phase's 4 copies may stay in flight; sub-tile ph+1 has landed
+    else
+      wait_vmem();
+    __syncthreads();
+  }
+
+  const float lt = swap_halves_sum(l[0]);
+  if (full) {
+    const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+    store_rows_f16(ro, row_base + col, half, acc[0], lt, 1.0f);
+  } else {
+    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+    const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
+    store_partial(rp, sbase, kRowsPerBlock, wave * 32 + col, half, acc[0], m[0], lt);
+  }
+}
+
+// Variant for 4 waves of 32 rows (128-row q-blocks, two workgroups per
+// compute unit): keys in 32-key sub-tiles through a 2-deep LDS ring (V at 0
+// and 16 KiB, K at 32 and 48 KiB).  The two waves that share a SIMD belong to
+// different workgroups, so their barriers are independent and one computes
+// while the other waits.
+__device__ __forceinline__ void prefill_piece_ring(const PrefillParams& p, char* smem, int b, int tile_lo,
+                                                   int tile_hi, bool full, int slot) {
+  constexpr int W = 4;
+  constexpr int kSub = 32;
+  constexpr int kSubBytes = kSub * kRowBytes;  // 16 KiB
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+  const uint32_t kl = 512u * half + 16u * (uint32_t)(col ^ half);
+  const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
+
+  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
+  const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes);
+  const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes);
+
+  const int row_base = b * kRowsPerBlock + wave * 32;
+  const bool wave_active = row_base < p.nrows;
+  const int wrow_hi = min(row_base + 31, p.nrows - 1);
+  const int wpos_lo = p.q_pos0 + row_base / kGroup;
+  const int wpos_hi = p.q_pos0 + wrow_hi / kGroup;
+
+  int pos[1];
+  h8 qf[1][16];
+  {
+    const int row = row_base + col;
+    pos[0] = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
+    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
+#pragma unroll
+    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
+  }
+  f16x acc[1][8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
+  float m[1] = {-INFINITY}, l[1] = {0.f};
+  uint32_t bk = k_lane_base(lane);
+  uint32_t bv = v_lane_base(lane);
+
+  const int n_sub = 2 * (tile_hi - tile_lo);
+  const int key_base = tile_lo * kTileKeys;
+  auto issue_sub = [&](int x) {
+    const int buf = x & 1;
+    issue_rows<W, kSub>(rk, rv, (uint32_t)(key_base + kSub * x) * kRowBytes, smem + (2 + buf) * kSubBytes,
+                        smem + buf * kSubBytes, wave, kl, vl);
+  };
+  if (n_sub > 0) issue_sub(0);
+  wait_vmem();
+  __syncthreads();
+  for (int ph = 0; ph < n_sub; ++ph) {
+    if (ph + 1 < n_sub) issue_sub(ph + 1);
+    asm volatile("" : "+v"(bk), "+v"(bv));
+    const int k0 = key_base + kSub * ph;
+    if (wave_active && k0 <= wpos_hi) {
+      const int buf = ph & 1;
+      attend_32keys<1>(lds_addr((const GQA_LDS char*)smem + (2 + buf) * kSubBytes) + bk,
+                       (const GQA_LDS char*)smem + buf * kSubBytes, bv, 0, qf, acc, m, l, p.c, k0 + 31 > wpos_lo,
+                       [&](int c, int vv) { return k0 + lane_key(vv, half) <= pos[c]; });
+    }
+    wait_vmem();
+    __syncthreads();
+  }
+
+  const float lt = swap_halves_sum(l[0]);
+  if (full) {
+    const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+    store_rows_f16(ro, row_base + col, half, acc[0], lt, 1.0f);
+  } else {
+    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+    const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
+    store_partial(rp, sbase, kRowsPerBlock, wave * 32 + col, half, acc[0], m[0], lt);
+  }
+}
+
+#ifndef GQA_PREFILL_PINGPONG
+#define GQA_PREFILL_PINGPONG 0
+#endif
+
 template <int C, int W>
-__global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
+__device__ __forceinline__ void prefill_run(const PrefillParams& p, char* smem, int b, int lo, int hi, bool full,
+                                            int slot) {
+  if constexpr (C == 1 && W == 4)
+    prefill_piece_ring(p, smem, b, lo, hi, full, slot);
+  else if constexpr (GQA_PREFILL_PINGPONG && C == 1 && W == 8)
+    prefill_piece_pingpong(p, smem, b, lo, hi, full, slot);
+  else
+    prefill_piece<C, W>(p, smem, b, lo, hi, full, slot);
+}
+
+template <int C, int W>
+__global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void prefill_causal_fwd(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[W == 4 ? 2 * kTileBytes : 4 * kTileBytes];
   const int w = blockIdx.x;
   if (p.split > 0) {
     const int b = w / p.split, j = w % p.split;
     const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
     const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
     // the split never exceeds the shortest q-block's tile count, so lo < hi
-    prefill_piece<C, W>(p, smem, b, lo, hi, p.split == 1, w);
+    prefill_run<C, W>(p, smem, b, lo, hi, p.split == 1, w);
     return;
   }
   long long t0 = prefill_range_start(w, p.total, p.grid);
@@ -217,7 +426,7 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p)
     const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
     const long long seg_end = cb + nt < t1 ? cb + nt : t1;
     const int lo = (int)(t0 - cb), hi = (int)(seg_end - cb);
-    prefill_piece<C, W>(p, smem, b, lo, hi, lo == 0 && hi == nt, w + b);
+    prefill_run<C, W>(p, smem, b, lo, hi, lo == 0 && hi == nt, w + b);
     t0 = seg_end;
     cb += nt;
     ++b;
@@ -228,8 +437,9 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p)
 // M = max_k m_k, O = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
 // Workgroup (b, quarter): 64 rows of q-block b; thread (row, 64 columns).
 __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
-  const int b = blockIdx.x >> 2;
-  const int quarter = blockIdx.x & 3;
+  constexpr int kParts = kRowsPerBlock / 64;
+  const int b = blockIdx.x / kParts;
+  const int quarter = blockIdx.x % kParts;
   int w0, w1, slot0;
   if (p.split > 0) {  // pieces of q-block b are slots b*split .. b*split + split - 1
     w0 = 0;
@@ -308,7 +518,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   prof_after(stream);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
-    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * 4), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / 64)), dim3(256), 0, stream, p);
     e = hipGetLastError();
   }
   return e;

@@ -23,7 +23,12 @@
 
 namespace gqa {
 
-constexpr int kRowsPerBlock = 256;  // packed rows per workgroup
+#ifndef GQA_PREFILL_ROWS
+#define GQA_PREFILL_ROWS 256
+#endif
+constexpr int kRowsPerBlock = GQA_PREFILL_ROWS;  // packed rows per workgroup (256: 8 waves, 128: 4 waves)
+// workgroups resident per compute unit (LDS: 128 KiB for 256 rows, 64 KiB for 128 rows)
+constexpr int kWGsPerCU = kRowsPerBlock == 256 ? 1 : 2;
 constexpr int kTileKeys = 64;       // keys per K/V tile
 constexpr int kTargetGrid = 256;    // one workgroup per MI355X compute unit
 constexpr int kMinTilesPerWG = 16;
@@ -88,15 +93,15 @@ inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
       if (nt < minnt) minnt = nt;
     }
     int sp = 1;
-    while (sp < 8 && (long long)s.nqb * sp < 2LL * kTargetGrid && sp * 2 <= minnt) sp *= 2;
+    while (sp < 8 && (long long)s.nqb * sp < 2LL * kTargetGrid * kWGsPerCU && sp * 2 <= minnt) sp *= 2;
     s.split = sp;
     s.grid = s.nqb * sp;
   }
   return s;
 }
 
-// Partial slot: fp32 O^T [256 d][256 rows], then m [256], then l [256].
-constexpr size_t kPartialFloats = (size_t)256 * 256 + 256 + 256;
+// Partial slot: fp32 acc [64 column quads][rows][4], then m [rows], then l [rows].
+constexpr size_t kPartialFloats = (size_t)kRowsPerBlock * 256 + 2 * kRowsPerBlock;
 
 // True when some q-block is cut between workgroups (its partials need merging).
 inline bool prefill_needs_merge(const PrefillSched& s) {

@@ -177,34 +177,40 @@ __global__ __launch_bounds__(256, 1) void verify_fwd(VerifyParams p) {
   }
 }
 
-// Workgroup r merges row r over all partial slots: thread (quad, lane4) takes
-// columns 4*quad .. 4*quad+3 of the slots lane4, lane4+4, ...
+// Merge of the workgroups' partials: workgroup (r, part) combines row r,
+// head-dim columns 64*part .. 64*part+63, over all slots.  Thread
+// (quad, sl) takes columns 64*part + 4*quad .. +3 of the slots sl, sl+16, ...;
+// the 16 slot lanes are then reduced through LDS.
 __global__ __launch_bounds__(256) void verify_merge(VerifyParams p) {
-  __shared__ float red[4][64][5];
-  __shared__ float mred[4];
-  const int r = blockIdx.x;
+  __shared__ float red[16][16][5];
+  __shared__ float mred[16];
+  const int r = blockIdx.x >> 2;
+  const int part = blockIdx.x & 3;
   const int tid = threadIdx.x;
-  const int quad = tid & 63;
-  const int sl = tid >> 6;
+  const int quad = tid & 15;
+  const int sl = tid >> 4;
   const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
   const uint32_t slot_bytes = (uint32_t)(kVerifySlotFloats * 4);
   const uint32_t m_off = (uint32_t)(kVerifySlotRows * kHeadDim * 4);
   float M = -INFINITY;
-  for (int s = sl; s < p.grid; s += 4)
+  for (int s = sl; s < p.grid; s += 16)
     M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, s * slot_bytes + m_off + r * 4, 0, 0)));
-  // reduce M over the four slot lanes (lane quad 0 of each wave holds it)
   if (quad == 0) mred[sl] = M;
   __syncthreads();
-  M = fmaxf(fmaxf(mred[0], mred[1]), fmaxf(mred[2], mred[3]));
+  M = mred[0];
+#pragma unroll
+  for (int i = 1; i < 16; ++i) M = fmaxf(M, mred[i]);
   f4 o = {0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int s = sl; s < p.grid; s += 4) {
+  const uint32_t qoff = (uint32_t)(((16 * part + quad) * kVerifySlotRows + r) * 16);
+#pragma unroll 4
+  for (int s = sl; s < p.grid; s += 16) {
     const uint32_t sb = s * slot_bytes;
     const float ms = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + r * 4, 0, 0));
     const float ls = __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kVerifySlotRows + r) * 4, 0, 0));
+    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + qoff, 0, 0);
     const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)((quad * kVerifySlotRows + r) * 16), 0, 0);
     o += a * __builtin_bit_cast(f4, x);
     L += a * ls;
   }
@@ -218,7 +224,7 @@ __global__ __launch_bounds__(256) void verify_merge(VerifyParams p) {
     f4 t = {0.f, 0.f, 0.f, 0.f};
     float lt = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+    for (int i = 0; i < 16; ++i) {
       t[0] += red[i][quad][0];
       t[1] += red[i][quad][1];
       t[2] += red[i][quad][2];
@@ -228,7 +234,7 @@ __global__ __launch_bounds__(256) void verify_merge(VerifyParams p) {
     const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
     const h2 lo = cvt2(t[0] * inv, t[1] * inv), hi = cvt2(t[2] * inv, t[3] * inv);
     const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-    store_8B(ro, (uint32_t)r * kRowBytes + quad * 8, h4{lo[0], lo[1], hi[0], hi[1]});
+    store_8B(ro, (uint32_t)r * kRowBytes + (16 * part + quad) * 8, h4{lo[0], lo[1], hi[0], hi[1]});
   }
 }
 
@@ -257,7 +263,7 @@ hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v
   hipError_t e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_merge, dim3(p.nrows), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(verify_merge, dim3(p.nrows * 4), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
