@@ -18,13 +18,23 @@ Prints ONE JSON line.  Besides the driver's fields it carries
   paths         the same measurement for the other entry points (paged
                 block-sparse prefill, FP8 verifier tail) when they are built.
 
+`roofline.traffic` is the HBM traffic per launch of that kernel, read from the
+committed counter summary (profiles/hbm_traffic_per_launch.md) when the kernel
+sources still hash to the digest recorded there, else null.  That summary is
+written by `python bench.py --summarize-counters FETCH.csv WRITE.csv` from two
+rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
+`bench.py --steps S --warmup W --no-cpu-baseline --copy-calibration-mib M`.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
 """
 
 from __future__ import annotations
 
 import argparse
+import csv
+import hashlib
 import json
+import re
 import os
 import sys
 import time
@@ -41,6 +51,114 @@ PEAK_F16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
 PEAK_HBM_GBS = 8000.0
 # The long-prefill page's candidate at this workload (V100, FP16): 100.20284 ms.
 PAGE_MS_Q8000_KV128000 = 100.20284
+
+
+TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_per_launch.md")
+PAGED_SELECTIONS = (64, 512, 2048)
+VERIFY_QUERIES = (2, 4, 8)
+
+
+def prefill_workload(n_kv: int) -> str:
+    return f"causal_gqa_prefill_q8000_kv{n_kv}"
+
+
+def paged_workload(select_tokens: int, tail: int = 1) -> str:
+    return f"paged_sparse_q4096_page16_select{select_tokens}_tail{tail}"
+
+
+def verify_workload(nq: int) -> str:
+    return f"verify_fp8kv_q{nq}_ctx{workloads.VERIFY_CONTEXT}"
+
+
+def kernel_source_digest() -> str:
+    """Hash of the kernel sources and of the build script (its flags shape the code)."""
+    h = hashlib.sha256()
+    pkg = os.path.join(ROOT, "gqa_causal_flash_amd")
+    csrc = os.path.join(pkg, "csrc")
+    files = [os.path.join(csrc, n) for n in sorted(os.listdir(csrc)) if n.endswith((".hip", ".hpp", ".cpp", ".h"))]
+    files.append(os.path.join(pkg, "build.py"))
+    for f in files:
+        h.update(os.path.basename(f).encode() + b"\0")
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic() -> dict:
+    """{(kernel, workload): HBM bytes per launch} from the committed counter summary,
+    or {} when it was taken on other kernel sources than these."""
+    try:
+        with open(TRAFFIC_TABLE) as f:
+            text = f.read()
+    except OSError:
+        return {}
+    m = re.search(r"kernel source digest: `([0-9a-f]+)`", text)
+    if not m or m.group(1) != kernel_source_digest():
+        return {}
+    out = {}
+    for line in text.splitlines():
+        cells = [c.strip().strip("`") for c in line.strip().strip("|").split("|")]
+        if len(cells) == 6 and cells[5].replace(",", "").isdigit():
+            out[(cells[0], cells[1])] = int(cells[5].replace(",", ""))
+    return out
+
+
+def _counter_rows(path: str, counter: str):
+    rows = []
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            if r["Counter_Name"] == counter:
+                m = re.search(r"gqa::\(anonymous namespace\)::(\w+)", r["Kernel_Name"])
+                name = m.group(1) if m else r["Kernel_Name"].split("(")[0].split()[-1]
+                rows.append((int(r["Dispatch_Id"]), name, float(r["Counter_Value"])))
+    rows.sort()
+    return rows
+
+
+def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, calib_mib: int, n_kv: int) -> str:
+    """Markdown table of FETCH_SIZE / WRITE_SIZE per launch of every libgqa kernel.
+
+    The three plain device copies of `calib_mib` MiB made before any workload are
+    the known-size reference: each counter's scale factor is the copy's true byte
+    count over what the counter reads for it.  Dispatches are assigned to
+    workloads by the benchmark's fixed order: a step starts at prefill_causal_fwd,
+    paged_prepass or verify_fwd, and each workload makes warmup + steps of them."""
+    per = warmup + steps
+    first = {"prefill_causal_fwd": "prefill", "paged_prepass": "paged", "verify_fwd": "verify"}
+    labels = {"prefill": [prefill_workload(n_kv)],
+              "paged": [paged_workload(s) for s in PAGED_SELECTIONS],
+              "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
+    true_kib = calib_mib * 1024.0
+    result, factors = {}, {}
+    for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
+        rows = _counter_rows(path, counter)
+        copies = [v for _, n, v in rows if n == "__amd_rocclr_copyBuffer"][:3]
+        if len(copies) < 3 or max(copies) > 1.01 * min(copies):
+            raise SystemExit(f"{path}: the first three copies do not look like the {calib_mib} MiB calibration: {copies}")
+        factors[counter] = true_kib / (sum(copies) / 3)
+        count = {k: 0 for k in labels}
+        cur = None
+        for _, name, v in rows:
+            if name in first:
+                cur = first[name]
+                count[cur] += 1
+            if cur is None or not name.startswith(cur):
+                continue
+            wl = labels[cur][min((count[cur] - 1) // per, len(labels[cur]) - 1)]
+            result.setdefault((name, wl), {}).setdefault(counter, []).append(v)
+    lines = [
+        "| kernel | workload | dispatches | FETCH_SIZE (KiB, avg) | WRITE_SIZE (KiB, avg) | HBM bytes per launch |",
+        "|---|---|---|---|---|---|",
+    ]
+    for (name, wl), c in result.items():
+        f = sum(c.get("FETCH_SIZE", [0])) / max(1, len(c.get("FETCH_SIZE", [])))
+        w = sum(c.get("WRITE_SIZE", [0])) / max(1, len(c.get("WRITE_SIZE", [])))
+        nbytes = (f * factors["FETCH_SIZE"] + w * factors["WRITE_SIZE"]) * 1024
+        lines.append(f"| `{name}` | `{wl}` | {len(c.get('FETCH_SIZE', []))} | {f:,.1f} | {w:,.1f} | {round(nbytes):,} |")
+    head = (f"kernel source digest: `{kernel_source_digest()}`\n\n"
+            f"calibration: plain device copy of {calib_mib} MiB; FETCH_SIZE scale {factors['FETCH_SIZE']:.4f}, "
+            f"WRITE_SIZE scale {factors['WRITE_SIZE']:.4f}\n\n")
+    return head + "\n".join(lines) + "\n"
 
 
 def prefill_flops(nq: int, n_kv: int, q_pos0: int, hq: int = 6, d: int = 256) -> float:
@@ -173,12 +291,13 @@ def bench_paged(select_tokens, steps, warmup, tail=1, seed=0):
     moved = gathered + 2 * x.q.nbytes
     tf = flops / (kms * 1e-3) / 1e12
     return {
-        "workload": f"paged_sparse_q4096_page16_select{select_tokens}_tail{tail}",
+        "workload": paged_workload(select_tokens, tail),
         "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "visible_pairs_per_head": pairs,
         "roofline": {"kernel": "paged_fwd", "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 4),
-                     "moved_GBps": round(moved / (kms * 1e-3) / 1e9, 1), "traffic": None},
+                     "moved_GBps": round(moved / (kms * 1e-3) / 1e9, 1),
+                     "traffic": recorded_traffic().get(("paged_fwd", paged_workload(select_tokens, tail)))},
         "page_ms_v100": {64: 1.010, 512: 3.204, 2048: 11.203}[select_tokens],
     }
 
@@ -207,10 +326,11 @@ def bench_verify(nq, steps, warmup, copies=3, seed=0):
     alg = 2 * x.k_bytes.nbytes + 2 * x.q.nbytes
     gbs = alg / (kms * 1e-3) / 1e9
     return {
-        "workload": f"verify_fp8kv_q{nq}_ctx{workloads.VERIFY_CONTEXT}",
+        "workload": verify_workload(nq),
         "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4), "kv_copies_rotated": copies,
         "roofline": {"kernel": "verify_fwd", "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "traffic": None},
+                     "unit": "GB/s", "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_bytes": alg,
+                     "traffic": recorded_traffic().get(("verify_fwd", verify_workload(nq)))},
     }
 
 
@@ -226,7 +346,15 @@ def main(argv=None):
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times), as the known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="print the per-launch HBM traffic table from two rocprofv3 --pmc counter_collection.csv "
+                         "files of a run made with the given --steps/--warmup/--kv/--copy-calibration-mib, and exit")
     args = ap.parse_args(argv)
+
+    if args.summarize_counters:
+        print(summarize_counters(*args.summarize_counters, steps=args.steps, warmup=args.warmup,
+                                 calib_mib=args.copy_calibration_mib or 1024, n_kv=args.kv), end="")
+        return 0
 
     if args.gpus != 1:
         print("bench.py: libgqa is a single-GPU library; this benchmark runs on exactly one GPU "
@@ -247,7 +375,7 @@ def main(argv=None):
             dst.copy_(src)
         torch.cuda.synchronize()
         print(f"copy calibration: 3 x {n} bytes", file=sys.stderr)
-    cfg = workloads.CausalConfig(f"causal_gqa_prefill_q8000_kv{args.kv}", nq=8000, n_kv=args.kv)
+    cfg = workloads.CausalConfig(prefill_workload(args.kv), nq=8000, n_kv=args.kv)
     r = bench_prefill(cfg, args.steps, args.warmup)
     value = r["flops"] / (r["ms"] * 1e-3) / 1e12
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
@@ -276,13 +404,14 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_F16_TFLOPS, 4),
             "kernel_ms": round(r["kernel_ms"], 4),
-            "traffic": None,
+            "algorithmic_bytes": 2 * (2 * cfg.nq * cfg.hq * cfg.d + 2 * cfg.n_kv * cfg.d),
+            "traffic": recorded_traffic().get(("prefill_causal_fwd", cfg.name)),
         },
     }
     if not args.no_paths:
         line["paths"] = {
-            "paged_sparse": [bench_paged(sel, args.steps, args.warmup) for sel in (64, 512, 2048)],
-            "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in (2, 4, 8)],
+            "paged_sparse": [bench_paged(sel, args.steps, args.warmup) for sel in PAGED_SELECTIONS],
+            "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in VERIFY_QUERIES],
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(cfg, r["host"], args.cpu_seconds)

@@ -400,8 +400,8 @@ __device__ __forceinline__ void prefill_run(const PrefillParams& p, char* smem, 
 }
 
 template <int C, int W>
-__global__ __launch_bounds__(64 * W, (W == 4 ? 2 : 1)) void prefill_causal_fwd(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[W == 4 ? 2 * kTileBytes : 4 * kTileBytes];
+__global__ __launch_bounds__(64 * W, (C == 1 && W == 4 ? 2 : 1)) void prefill_causal_fwd(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[(C == 1 && W == 4) ? 2 * kTileBytes : 4 * kTileBytes];
   const int w = blockIdx.x;
   if (p.split > 0) {
     const int b = w / p.split, j = w % p.split;
