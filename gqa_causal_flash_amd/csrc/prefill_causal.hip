@@ -10,11 +10,12 @@
 // through a 750-MiB score workspace) is not followed: scores never leave the
 // registers.
 //
-// Workgroup: 4 waves (one per SIMD) x 64 packed rows = 256 rows (a q-block).
-// Each wave keeps its 64 rows of Q as matrix-core B fragments in registers
-// (2 column blocks of 32 rows x 16 steps of 16 head-dim columns) and its
-// O^T accumulator (2 x 8 tiles of 32x32 fp32).  K/V tiles of 64 keys stream
-// HBM -> LDS by direct-to-LDS loads into a double buffer (2 x 64 KiB).
+// Workgroup: 8 waves (two per SIMD) x 32 packed rows = 256 rows (a q-block).
+// Each wave keeps its 32 rows of Q as matrix-core B fragments in registers
+// (16 steps of 16 head-dim columns) and its O^T accumulator (8 tiles of 32x32
+// fp32).  K/V tiles of 64 keys stream HBM -> LDS by direct-to-LDS loads into a
+// double buffer (2 x 64 KiB).  (Templates C and W give other row splits,
+// 32C rows per wave and W waves, kept for measurement.)
 #include "attn_common.hpp"
 #include "attn_tile.hpp"
 #include "prefill_sched.hpp"
@@ -404,11 +405,13 @@ __global__ __launch_bounds__(64 * W, (C == 1 && W == 4 ? 2 : 1)) void prefill_ca
   __shared__ __attribute__((aligned(1024))) char smem[(C == 1 && W == 4) ? 2 * kTileBytes : 4 * kTileBytes];
   const int w = blockIdx.x;
   if (p.split > 0) {
-    const int b = w / p.split, j = w % p.split;
+    // q-blocks are dispatched last first: they are the longest, so the
+    // shortest pieces end the kernel
+    const int b = p.nqb - 1 - w / p.split, j = w % p.split;
     const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
     const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
     // the split never exceeds the shortest q-block's tile count, so lo < hi
-    prefill_run<C, W>(p, smem, b, lo, hi, p.split == 1, w);
+    prefill_run<C, W>(p, smem, b, lo, hi, p.split == 1, b * p.split + j);
     return;
   }
   long long t0 = prefill_range_start(w, p.total, p.grid);

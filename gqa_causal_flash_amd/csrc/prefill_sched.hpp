@@ -6,7 +6,7 @@
 // tall GEMM against each K/V tile (the head packing of the long-prefill page,
 // Purpose).
 //
-// A q-block is 256 consecutive packed rows (one workgroup, four waves of 64).
+// A q-block is 256 consecutive packed rows (one workgroup, eight waves of 32).
 // Its key range is 0 .. pmax (the position of its last row), cut into 64-key
 // tiles.  Laying the q-blocks' tiles end to end gives a line of T tiles that
 // is split evenly over G workgroups (workgroup w takes tiles floor(wT/G) ..
@@ -61,11 +61,12 @@ __host__ __device__ inline int prefill_owner(long long x, long long total, int g
 
 // Key-split mode (used when split > 0): q-block b's tiles are cut into `split`
 // equal key ranges, piece j = tiles floor(j n_b / split) .. floor((j+1) n_b /
-// split) - 1, and workgroup u = b * split + j runs piece j of q-block b.  With
-// split dividing 8, the round-robin placement of workgroup u on XCD u % 8 puts
-// only piece u % split on each XCD, so the 32 workgroups of an XCD stream the
-// same K/V range at the same pace and share that XCD's L2.  Piece j of q-block
-// b leaves its partial in slot u.
+// split) - 1, and workgroup u = (nqb - 1 - b) * split + j runs piece j of
+// q-block b (the longest q-blocks, the last ones, go first).  With split
+// dividing 8, the round-robin placement of workgroup u on XCD u % 8 puts only
+// piece u % split on each XCD, so the 32 workgroups of an XCD stream the same
+// K/V range at the same pace and share that XCD's L2.  Piece j of q-block b
+// leaves its partial in slot b * split + j.
 #ifndef GQA_PREFILL_KEYSPLIT
 #define GQA_PREFILL_KEYSPLIT 1
 #endif
