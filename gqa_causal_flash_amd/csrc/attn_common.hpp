@@ -133,6 +133,18 @@ __device__ __forceinline__ float swap_halves_sum(float x) {
   return __uint_as_float(p[0]) + __uint_as_float(p[1]);
 }
 
+// Workgroup barrier for loops that keep loads into LDS in flight across it.
+// __syncthreads() fences memory, and a release of LDS waits for every
+// outstanding load into LDS as well; here those loads are waited for
+// explicitly, as far as each step needs.  This barrier waits only for the
+// wave's own LDS reads and writes (lgkmcnt), and the empty asm statements
+// with a memory clobber keep the compiler from moving memory accesses across.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ f16x mfma(h8 a, h8 b, f16x c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }

@@ -6,29 +6,41 @@
 // of up to 262144 tokens stored as E4M3 bytes, with fp32 accumulation.  The
 // page decodes E4M3 through a shared-memory lookup table because its GPU has
 // no FP8 unit; gfx950 converts in hardware (v_cvt_scalef32_pk_f16_fp8), and
-// every E4M3 value is exact in fp16, so the decoded tiles feed the same fp16
-// matrix-core step as the dense kernel.  The per-tensor K scale is folded into
-// the softmax scale and the V scale into the final normalisation.
+// every E4M3 value is exact in fp16, so the decoded fragments feed the same
+// fp16 matrix-core step as the dense kernel.  The per-tensor K scale is folded
+// into the softmax scale and the V scale into the final normalisation.
 //
 // The work is bound by HBM bandwidth (K + V = 512 B per key), so the key range
-// is split over every compute unit: each workgroup runs two independent key
-// streams of two waves (one per 32-row block of the <= 48 packed query rows);
-// a stream prefetches the raw bytes of its next 32-key tile into registers
-// while it decodes and attends the current one.  The two streams of a
-// workgroup are merged in LDS and written as one online-softmax partial; a
-// second kernel merges the workgroups' partials by log-sum-exp.
+// is split evenly over two workgroups per compute unit.  A workgroup (two
+// waves, one per 32-row block of the <= 48 packed query rows) streams its
+// keys in 32-key tiles of raw bytes through a ring of kRing LDS slots with
+// direct HBM -> LDS loads, kRing - 1 tiles ahead of the one it computes, so
+// each compute unit keeps 128 KiB of loads in flight.  The bytes are decoded
+// to fp16 in registers, right where the matrix cores take them:
+//   K fragments (S^T = K Q^T, A operand) by an 8-byte LDS read per lane;
+//     the head-dimension order of the product is permuted so that lane half h
+//     covers columns 128h .. 128h+127 (Q is loaded in the same order);
+//   V^T fragments (O^T += V^T P^T, A operand) by the transposing read
+//     ds_read_b64_tr_b8, which hands each lane eight consecutive keys of one
+//     head-dimension column.
+// Each workgroup writes one online-softmax partial; a second kernel merges the
+// partials by log-sum-exp.
 #include "attn_common.hpp"
 #include "attn_tile.hpp"
 #include "launch.hpp"
 #include "verify_sched.hpp"
+
+#include <type_traits>
 
 namespace gqa {
 
 namespace {
 
 constexpr int kVTileKeys = 32;
-constexpr int kVTileBytes = kVTileKeys * kRowBytes;  // fp16 tile: 16 KiB
-constexpr int kFp8Row = kHeadDim;                    // bytes per E4M3 row
+constexpr int kFp8Row = kHeadDim;                     // bytes per E4M3 row
+constexpr int kRawTile = kVTileKeys * kFp8Row;        // 8 KiB of K or V bytes
+constexpr int kRing = 5;                              // LDS slots of K + V raw tiles
+constexpr int kSlotBytes = 2 * kRawTile;              // 16 KiB: K at 0, V at 8 KiB
 
 struct VerifyParams {
   const _Float16* q;
@@ -36,154 +48,184 @@ struct VerifyParams {
   const uint8_t* v;
   _Float16* o;
   float* part;
-  int nq, nrows, n_kv, ntiles, nstreams, grid;
+  int nq, nrows, n_kv, ntiles, grid;
   uint32_t part_bytes;
   float c;        // scale * k_scale * log2(e)
   float v_scale;
 };
 
-// Decode 16 E4M3 bytes (one 16-byte chunk: head-dim columns 16cb .. 16cb+15 of
-// a row) into two fp16 chunks and store them at their swizzled LDS places.
-__device__ __forceinline__ void decode_store(u4 raw, GQA_LDS char* row_base, int cb, int phys0, int phys1) {
-  h8 lo, hi;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[w], 1.0f, false);
-    const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[w], 1.0f, true);
-    h8& dst = (w < 2) ? lo : hi;
-    const int o = 4 * (w & 1);
-    dst[o + 0] = a[0];
-    dst[o + 1] = a[1];
-    dst[o + 2] = b[0];
-    dst[o + 3] = b[1];
-  }
-  (void)cb;
-  *(GQA_LDS h8*)(row_base + phys0 * 16) = lo;
-  *(GQA_LDS h8*)(row_base + phys1 * 16) = hi;
+// Raw tile layout in LDS: row r of a tile (256 bytes = 16 chunks of 16 B)
+// keeps logical chunk c at physical chunk c ^ swz(r), with swz = r % 16 for K
+// and 2 ((r % 4) + 4 ((r / 8) % 2)) for V, so that the fragment reads below
+// spread over the banks (the eight V rows one transposing read takes differ
+// in bits 0, 1 and 3).
+__device__ __forceinline__ uint32_t k_swz(int r) { return (uint32_t)(r & 15); }
+__device__ __forceinline__ uint32_t v_swz(int r) { return 2u * (uint32_t)((r & 3) | (((r >> 3) & 1) << 2)); }
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+
+// 8 E4M3 bytes -> 8 fp16 values (exact), in byte order.
+__device__ __forceinline__ h8 decode8(v2i raw) {
+  const h2 a = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw[0], 1.0f, false);
+  const h2 b = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw[0], 1.0f, true);
+  const h2 c = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw[1], 1.0f, false);
+  const h2 d = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8((unsigned)raw[1], 1.0f, true);
+  return h8{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
 }
 
-__global__ __launch_bounds__(256, 1) void verify_fwd(VerifyParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[2][2][2 * kVTileBytes];  // [stream][buf][K | V]
+// The ring slots are separate LDS arrays, and the loop is unrolled over the
+// ring so that every slot index is a compile-time constant: the compiler can
+// then see that the fragment reads of one slot do not touch the slots that
+// loads are in flight into, and inserts no wait for those loads (it would if
+// all slots lived in one array).  Completion is waited for explicitly.
+struct RawRing {
+  char* s[kRing];
+};
+
+__global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
+  __shared__ __attribute__((aligned(1024))) char r0[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char r1[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char r2[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char r3[kSlotBytes];
+  __shared__ __attribute__((aligned(1024))) char r4[kSlotBytes];
+  static_assert(kRing == 5, "one array per slot");
+  const RawRing ring = {{r0, r1, r2, r3, r4}};
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int stream = wave >> 1;
-  const int cblk = wave & 1;  // row block 0 (rows 0..31) or 1 (rows 32..63); also K (0) / V (1) loader
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // row block; also K (0) / V (1) loader
   const int half = lane >> 5;
   const int col = lane & 31;
+  (void)tid;
 
-  const int sid = 2 * blockIdx.x + stream;
-  const int t_lo = (int)((long long)sid * p.ntiles / p.nstreams);
-  const int t_hi = (int)((long long)(sid + 1) * p.ntiles / p.nstreams);
-  // the two streams may differ by one tile; every wave runs the longer count
-  // of iterations so that all of them meet at the same barriers
-  const int s0 = 2 * blockIdx.x;
-  const int n0 = (int)((long long)(s0 + 1) * p.ntiles / p.nstreams) - (int)((long long)s0 * p.ntiles / p.nstreams);
-  const int n1 = (int)((long long)(s0 + 2) * p.ntiles / p.nstreams) -
-                 (int)((long long)(s0 + 1) * p.ntiles / p.nstreams);
-  const int n_iter = n0 > n1 ? n0 : n1;
+  const int t_lo = (int)((long long)blockIdx.x * p.ntiles / p.grid);
+  const int t_hi = (int)((long long)(blockIdx.x + 1) * p.ntiles / p.grid);
+  const int n = t_hi - t_lo;  // >= 1
 
-  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
-  const rsrc_t rsrc_kv = make_rsrc(cblk == 0 ? (const void*)p.k : (const void*)p.v, (uint32_t)p.n_kv * kFp8Row);
+  // this wave's loads: raw tile rows 4i .. 4i+3 per instruction, lane l taking
+  // row 4i + l/16 and physical chunk l % 16 (logical chunk (l % 16) ^ swz)
+  const rsrc_t rkv = make_rsrc(wave == 0 ? (const void*)p.k : (const void*)p.v, (uint32_t)p.n_kv * kFp8Row);
+  uint32_t loff[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int r = 4 * i + (lane >> 4);
+    const uint32_t swz = wave == 0 ? k_swz(r) : v_swz(r);
+    loff[i] = (uint32_t)r * kFp8Row + 16u * ((uint32_t)(lane & 15) ^ swz);
+  }
+  auto issue = [&](char* slot, int t) {  // raw bytes of tile t into a slot
+    GQA_LDS char* dst = (GQA_LDS char*)slot + wave * kRawTile;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) load_lds_16B(rkv, dst + i * 1024, loff[i], (uint32_t)t * kRawTile);
+  };
 
-  const int row = 32 * cblk + col;
-  const bool rows_active = 32 * cblk < p.nrows;
+  const int row = 32 * wave + col;
+  const bool rows_active = 32 * wave < p.nrows;
   const int pos = (p.n_kv - p.nq) + min(row, p.nrows - 1) / kGroup;
   const int pos_min = p.n_kv - p.nq;  // first query position
+  // Q as B fragments in the permuted column order: step s, lane half h holds
+  // columns 128h + 8s .. 128h + 8s + 7
   h8 qf[1][16];
   {
-    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
+    const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
+    const uint32_t qoff = (uint32_t)row * kRowBytes + 256u * half;
 #pragma unroll
-    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
+    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + 16u * s);
   }
   f16x acc[1][8];
 #pragma unroll
   for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
   float m[1] = {-INFINITY}, l[1] = {0.f};
-  uint32_t bk = k_lane_base(lane);
-  uint32_t bv = v_lane_base(lane);
 
-  // this wave stages K (cblk 0) or V (cblk 1) of its stream: load j covers
-  // row 4j + lane/16, byte chunk lane%16
-  const int cb = lane & 15;
-  u4 raw[8];
-  auto load_raw = [&](int t) {
+  // K fragment s of lane (key r = col, half h): bytes 128h + 8s .. +7 of row r,
+  // logical chunk 8h + s/2, byte 8 (s % 2)
+  uint32_t kbase = (uint32_t)col * kFp8Row;
+  // V^T fragment (dt, key half t): the product's key order is that of P^T as
+  // it leaves the score registers: element e of lane half h is key
+  // 16t + 8(e/4) + 4h + e%4.  ds_read_b64_tr_b8 gives output lane i, element e
+  // byte i of the 16 bytes that source lanes 2e and 2e+1 of its 16-lane group
+  // address, so source lane k of group g (half h = g/2) addresses key
+  // 16t + 8(k/8) + 4h + (k/2)%4 at columns 32dt + 16(g%2) + 8(k%2), i.e.
+  // logical chunk 2dt + g%2, byte 8(k%2).
+  const int g = lane >> 4, sk = lane & 15;
+  const int vrow0 = 8 * (sk >> 3) + 4 * (g >> 1) + ((sk >> 1) & 3);  // + 16t
+  const uint32_t vswz = v_swz(vrow0);                                 // (16t keeps the swizzle)
+  uint32_t vbase = (uint32_t)vrow0 * kFp8Row + 8u * (sk & 1);
+
+  // prologue: kRing - 1 tiles in flight, tile j in slot j
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      raw[j] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_kv, (uint32_t)t * (kVTileKeys * kFp8Row) +
-                                                                  (uint32_t)((4 * j + (lane >> 4)) * kFp8Row + 16 * cb),
-                                                     0, 0);
-  };
-  if (t_lo < t_hi) load_raw(t_lo);
+  for (int j = 0; j < kRing - 1; ++j)
+    if (j < n) issue(ring.s[j], t_lo + j);
 
-  for (int it = 0; it < n_iter; ++it) {
+  // iteration it computes tile t_lo + it from slot it % kRing
+  auto step = [&](auto slotc, int it) {
+    constexpr int SL = decltype(slotc)::value;
     const int t = t_lo + it;
-    const bool live = t < t_hi;  // wave-uniform
-    const int buf = it & 1;
-    GQA_LDS char* kt = (GQA_LDS char*)smem[stream][buf];
-    GQA_LDS char* vt = kt + kVTileBytes;
-    if (live) {
-      GQA_LDS char* dst = cblk == 0 ? kt : vt;
+    // tile t has landed once at most min(n - 1 - it, kRing - 2) later tiles are outstanding
+    const int later = min(n - 1 - it, kRing - 2);
+    if (later >= 3)
+      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+    else if (later == 2)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+    else if (later == 1)
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    lds_barrier();  // both halves of tile t are in; the slot of tile t-1 is free
+    if (it + kRing - 1 < n) issue(ring.s[(SL + kRing - 1) % kRing], t + kRing - 1);
+    if (rows_active) {
+      const GQA_LDS char* kt = (const GQA_LDS char*)ring.s[SL];
+      const GQA_LDS char* vt = kt + kRawTile;
+      const int k0 = t * kVTileKeys;
+      asm volatile("" : "+v"(kbase), "+v"(vbase));
+      // S^T = K Q^T
+      f16x s1[1];
+      s1[0] = f16x{};
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int r = 4 * j + (lane >> 4);
-        const int c0 = 2 * cb, c1 = 2 * cb + 1;
-        const int p0 = cblk == 0 ? k_phys_chunk(c0, r) : v_phys_chunk(c0, r);
-        const int p1 = cblk == 0 ? k_phys_chunk(c1, r) : v_phys_chunk(c1, r);
-        decode_store(raw[j], dst + r * kRowBytes, cb, p0, p1);
+      for (int si = 0; si < 16; ++si) {
+        const uint32_t ch = (uint32_t)(8 * half + (si >> 1)) ^ k_swz(col);
+        const v2i raw = *(const GQA_LDS v2i*)(kt + kbase + 16u * ch + 8u * (si & 1));
+        s1[0] = mfma(decode8(raw), qf[0][si], s1[0]);
+      }
+      h8 pk[1][2];
+      softmax_32keys<1>(s1, acc, m, l, p.c, k0 + 31 > pos_min,
+                        [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; }, pk);
+      // O^T += V^T P^T
+#pragma unroll
+      for (int st = 0; st < 16; ++st) {
+        const int dt = st >> 1, tt = st & 1;
+        const uint32_t ch = (uint32_t)(2 * dt + (g & 1)) ^ vswz;
+        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+            (GQA_LDS v2i*)(vt + vbase + (uint32_t)(16 * tt) * kFp8Row + 16u * ch));
+        acc[0][dt] = mfma(decode8(raw), pk[0][tt], acc[0][dt]);
       }
     }
-    if (t + 1 < t_hi) load_raw(t + 1);
-    __syncthreads();
-    if (live && rows_active) {
-      const int k0 = t * kVTileKeys;
-      asm volatile("" : "+v"(bk), "+v"(bv));
-      attend_32keys<1>(lds_addr(kt) + bk, vt, bv, 0, qf, acc, m, l, p.c, k0 + 31 > pos_min,
-                       [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; });
-    }
+  };
+  for (int it = 0; it < n; it += kRing) {
+    step(std::integral_constant<int, 0>{}, it);
+    if (it + 1 >= n) break;
+    step(std::integral_constant<int, 1>{}, it + 1);
+    if (it + 2 >= n) break;
+    step(std::integral_constant<int, 2>{}, it + 2);
+    if (it + 3 >= n) break;
+    step(std::integral_constant<int, 3>{}, it + 3);
+    if (it + 4 >= n) break;
+    step(std::integral_constant<int, 4>{}, it + 4);
   }
 
-  // merge stream 1 into stream 0 through LDS, then write one partial per workgroup
-  float lt = swap_halves_sum(l[0]);
-  __syncthreads();
-  float* xch = (float*)smem;  // [2 row blocks][128 floats of acc per lane group][64 lanes] + m, l
-  if (stream == 1) {
-    float* base = xch + cblk * (130 * 64);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) base[(dt * 16 + vv) * 64 + lane] = acc[0][dt][vv];
-    base[128 * 64 + lane] = m[0];
-    base[129 * 64 + lane] = lt;
-  }
-  __syncthreads();
-  if (stream == 0 && rows_active) {
-    const float* base = xch + cblk * (130 * 64);
-    const float m1 = base[128 * 64 + lane];
-    const float l1 = base[129 * 64 + lane];
-    const float mm = fmaxf(m[0], m1);
-    const float a0 = (m[0] == -INFINITY) ? 0.f : fast_exp2(m[0] - mm);
-    const float a1 = (m1 == -INFINITY) ? 0.f : fast_exp2(m1 - mm);
-#pragma unroll
-    for (int dt = 0; dt < 8; ++dt)
-#pragma unroll
-      for (int vv = 0; vv < 16; ++vv) acc[0][dt][vv] = a0 * acc[0][dt][vv] + a1 * base[(dt * 16 + vv) * 64 + lane];
-    lt = a0 * lt + a1 * l1;
-    if (row < p.nrows) {
-      const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-      store_partial(rp, (uint32_t)blockIdx.x * (uint32_t)(kVerifySlotFloats * 4), kVerifySlotRows, row, half,
-                    acc[0], mm, lt);
-    }
+  if (rows_active && row < p.nrows) {
+    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+    store_partial(rp, (uint32_t)blockIdx.x * (uint32_t)(kVerifySlotFloats * 4), kVerifySlotRows, row, half, acc[0],
+                  m[0], swap_halves_sum(l[0]));
   }
 }
 
 // Merge of the workgroups' partials: workgroup (r, part) combines row r,
-// head-dim columns 64*part .. 64*part+63, over all slots.  Thread
-// (quad, sl) takes columns 64*part + 4*quad .. +3 of the slots sl, sl+16, ...;
-// the 16 slot lanes are then reduced through LDS.
-__global__ __launch_bounds__(256) void verify_merge(VerifyParams p) {
-  __shared__ float red[16][16][5];
-  __shared__ float mred[16];
+// head-dim columns 64*part .. 64*part+63, over all slots in one pass.  Thread
+// (quad, sl) takes columns 64*part + 4*quad .. +3 of the slots sl, sl+32, ...,
+// keeping a running maximum and rescaling its sums when the maximum grows;
+// the 32 slot lanes are then combined the same way through LDS.
+constexpr int kMergeLanes = 32;
+__global__ __launch_bounds__(16 * kMergeLanes) void verify_merge(VerifyParams p) {
+  __shared__ float red[kMergeLanes][16][6];
   const int r = blockIdx.x >> 2;
   const int part = blockIdx.x & 3;
   const int tid = threadIdx.x;
@@ -192,44 +234,48 @@ __global__ __launch_bounds__(256) void verify_merge(VerifyParams p) {
   const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
   const uint32_t slot_bytes = (uint32_t)(kVerifySlotFloats * 4);
   const uint32_t m_off = (uint32_t)(kVerifySlotRows * kHeadDim * 4);
-  float M = -INFINITY;
-  for (int s = sl; s < p.grid; s += 16)
-    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, s * slot_bytes + m_off + r * 4, 0, 0)));
-  if (quad == 0) mred[sl] = M;
-  __syncthreads();
-  M = mred[0];
-#pragma unroll
-  for (int i = 1; i < 16; ++i) M = fmaxf(M, mred[i]);
-  f4 o = {0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
   const uint32_t qoff = (uint32_t)(((16 * part + quad) * kVerifySlotRows + r) * 16);
-#pragma unroll 4
-  for (int s = sl; s < p.grid; s += 16) {
+  float M = -INFINITY, L = 0.f;
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+  for (int s = sl; s < p.grid; s += kMergeLanes) {
     const uint32_t sb = s * slot_bytes;
     const float ms = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + r * 4, 0, 0));
     const float ls = __uint_as_float(
         __builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kVerifySlotRows + r) * 4, 0, 0));
-    const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + qoff, 0, 0);
+    const f4 x = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rp, sb + qoff, 0, 0));
+    if (ms > M) {  // rescale what was summed so far to the new maximum
+      const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - ms);
+      o *= a;
+      L *= a;
+      M = ms;
+    }
     const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    o += a * __builtin_bit_cast(f4, x);
+    o += a * x;
     L += a * ls;
   }
-  red[sl][quad][0] = o[0];
-  red[sl][quad][1] = o[1];
-  red[sl][quad][2] = o[2];
-  red[sl][quad][3] = o[3];
-  red[sl][quad][4] = L;
+  red[sl][quad][0] = M;
+  red[sl][quad][1] = L;
+  red[sl][quad][2] = o[0];
+  red[sl][quad][3] = o[1];
+  red[sl][quad][4] = o[2];
+  red[sl][quad][5] = o[3];
   __syncthreads();
   if (sl == 0) {
+    float Mt = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < kMergeLanes; ++i) Mt = fmaxf(Mt, red[i][quad][0]);
     f4 t = {0.f, 0.f, 0.f, 0.f};
     float lt = 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      t[0] += red[i][quad][0];
-      t[1] += red[i][quad][1];
-      t[2] += red[i][quad][2];
-      t[3] += red[i][quad][3];
-      lt += red[i][quad][4];
+    for (int i = 0; i < kMergeLanes; ++i) {
+      const float mi = red[i][quad][0];
+      const float a = (mi == -INFINITY) ? 0.f : fast_exp2(mi - Mt);
+      lt += a * red[i][quad][1];
+      t[0] += a * red[i][quad][2];
+      t[1] += a * red[i][quad][3];
+      t[2] += a * red[i][quad][4];
+      t[3] += a * red[i][quad][5];
     }
     const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
     const h2 lo = cvt2(t[0] * inv, t[1] * inv), hi = cvt2(t[2] * inv, t[3] * inv);
@@ -253,17 +299,16 @@ hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v
   p.nrows = nq * hq;
   p.n_kv = n_kv;
   p.ntiles = s.ntiles;
-  p.nstreams = 2 * s.grid;
   p.grid = s.grid;
   p.part_bytes = (uint32_t)verify_workspace_bytes(s);
   p.c = scale * k_scale * kLog2e;
   p.v_scale = v_scale;
   prof_before(stream);
-  hipLaunchKernelGGL(verify_fwd, dim3(s.grid), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(verify_fwd, dim3(s.grid), dim3(128), 0, stream, p);
   hipError_t e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(verify_merge, dim3(p.nrows * 4), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(verify_merge, dim3(p.nrows * 4), dim3(16 * kMergeLanes), 0, stream, p);
   return hipGetLastError();
 }
 

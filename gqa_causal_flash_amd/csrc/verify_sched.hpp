@@ -1,9 +1,9 @@
 // Work split of the FP8 verifier tail (host + device).
 //
-// Keys are cut into 32-key tiles; the tiles are spread evenly over
-// 2 * grid key streams (two per workgroup), with at least kVerifyMinTiles
-// tiles per stream where the key count allows, and at most one workgroup per
-// compute unit.  Each workgroup leaves one partial slot of kVerifySlotRows rows.
+// Keys are cut into 32-key tiles; the tiles are spread evenly over the
+// workgroups (one key stream each, two per compute unit), with at least
+// kVerifyMinTiles tiles per workgroup where the key count allows.  Each
+// workgroup leaves one partial slot of kVerifySlotRows rows.
 #pragma once
 
 #include <stddef.h>
@@ -14,7 +14,7 @@ constexpr int kVerifyMaxRows = 48;  // 8 query rows x 6 heads
 constexpr int kVerifyMaxContext = 262144;
 constexpr int kVerifySlotRows = 64;
 constexpr size_t kVerifySlotFloats = (size_t)kVerifySlotRows * 256 + 2 * kVerifySlotRows;
-constexpr int kVerifyMaxGrid = 256;
+constexpr int kVerifyMaxGrid = 512;
 constexpr int kVerifyMinTiles = 8;
 
 struct VerifySched {
@@ -27,9 +27,8 @@ inline VerifySched verify_schedule(int nq, int n_kv, int hq) {
   (void)hq;
   VerifySched s;
   s.ntiles = (n_kv + 31) / 32;
-  int streams = s.ntiles / kVerifyMinTiles;
-  if (streams < 2) streams = 2;
-  int g = (streams + 1) / 2;
+  int g = s.ntiles / kVerifyMinTiles;
+  if (g < 1) g = 1;
   if (g > kVerifyMaxGrid) g = kVerifyMaxGrid;
   s.grid = g;
   return s;
