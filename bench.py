@@ -12,7 +12,9 @@ Prints ONE JSON line.  Besides the driver's fields it carries
   roofline      the dominant kernel's achieved TFLOP/s (algorithmic FLOPs per
                 launch / its average duration, timed with HIP events recorded
                 by the library around that kernel on its stream) against the
-                fp16 dense matrix-core peak;
+                fp16 dense matrix-core peak; also the average shader clock those
+                launches ran at (sampled by the kernel while profiling) and the
+                fraction of the peak rescaled to that clock;
   cpu_baseline  the fp64 oracle timed on this host's cores for a bounded sample
                 of query rows of the same workload, in the same unit;
   paths         the same measurement for the other entry points (paged
@@ -48,6 +50,7 @@ if ROOT not in sys.path:
 import workloads  # noqa: E402
 
 PEAK_F16_TFLOPS = 2516.6  # 256 CUs x 2.4 GHz x 4096 dense fp16 FLOP/clk/CU
+PEAK_CLOCK_MHZ = 2400.0
 PEAK_HBM_GBS = 8000.0
 # The long-prefill page's candidate at this workload (V100, FP16): 100.20284 ms.
 PAGE_MS_Q8000_KV128000 = 100.20284
@@ -197,6 +200,7 @@ def time_steps(fn, steps: int, warmup: int):
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
     kms, kn = g.gqa_profile_stop()
+    time_steps.clock_mhz = g.gqa_profile_clock_mhz()
     return wall, (kms / kn if kn else float("nan"))
 
 
@@ -216,7 +220,7 @@ def bench_prefill(cfg, steps, warmup, seed=0):
 
     ms, kms = time_steps(step, steps, warmup)
     flops = prefill_flops(cfg.nq, cfg.n_kv, cfg.q_pos0)
-    return dict(ms=ms, kernel_ms=kms, flops=flops, host=(q, k, v))
+    return dict(ms=ms, kernel_ms=kms, flops=flops, host=(q, k, v), clock_mhz=time_steps.clock_mhz)
 
 
 def cpu_baseline_prefill(cfg, host, seconds: float):
@@ -404,6 +408,11 @@ def main(argv=None):
             "unit": "TFLOP/s",
             "frac": round(achieved / PEAK_F16_TFLOPS, 4),
             "kernel_ms": round(r["kernel_ms"], 4),
+            # the same launches against the peak rescaled to the shader clock they ran at
+            "clock_mhz": round(r["clock_mhz"], 1),
+            "peak_at_clock": round(PEAK_F16_TFLOPS * r["clock_mhz"] / PEAK_CLOCK_MHZ, 1) if r["clock_mhz"] else None,
+            "frac_at_clock": round(achieved / (PEAK_F16_TFLOPS * r["clock_mhz"] / PEAK_CLOCK_MHZ), 4)
+            if r["clock_mhz"] else None,
             "algorithmic_bytes": 2 * (2 * cfg.nq * cfg.hq * cfg.d + 2 * cfg.n_kv * cfg.d),
             "traffic": recorded_traffic().get(("prefill_causal_fwd", cfg.name)),
         },

@@ -33,6 +33,7 @@ SIGNATURES = {
     "gqa_verify_fp8kv": (_i32, [_vp, _vp, _vp, _f32, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
     "gqa_profile_start": (_i32, []),
     "gqa_profile_stop": (_i32, [ctypes.POINTER(ctypes.c_double), _i32p]),
+    "gqa_profile_clock_mhz": (_i32, [ctypes.POINTER(ctypes.c_double)]),
     "gqa_status_string": (ctypes.c_char_p, [_i32]),
     "gqa_last_hip_error": (ctypes.c_int, []),
     "gqa_abi_version": (ctypes.c_int, []),
@@ -147,6 +148,13 @@ def gqa_profile_stop():
     n = ctypes.c_int32(0)
     _check(lib().gqa_profile_stop(ctypes.byref(ms), ctypes.byref(n)), "gqa_profile_stop")
     return ms.value, n.value
+
+
+def gqa_profile_clock_mhz():
+    """Average shader clock (MHz) of the dense prefill kernels of the last stopped profiling session (0 if none)."""
+    mhz = ctypes.c_double(0.0)
+    _check(lib().gqa_profile_clock_mhz(ctypes.byref(mhz)), "gqa_profile_clock_mhz")
+    return mhz.value
 
 
 # ------------------------------------------------------ paged block-sparse

@@ -55,6 +55,9 @@ struct Profiler {
   bool on = false;
   std::vector<hipEvent_t> pool;   // created events, reused across sessions
   std::vector<hipEvent_t> marks;  // start/stop pairs of this session
+  unsigned long long* clk = nullptr;  // device {cycles, wall ticks}, 16 bytes
+  int clk_device = -1;
+  double last_mhz = 0.0;              // average shader clock of the last session
 };
 thread_local Profiler g_prof;
 
@@ -75,6 +78,7 @@ void prof_before(hipStream_t stream) {
   hipEvent_t e = prof_event();
   if (e && hipEventRecord(e, stream) == hipSuccess) g_prof.marks.push_back(e);
 }
+unsigned long long* prof_clock() { return g_prof.on ? g_prof.clk : nullptr; }
 void prof_after(hipStream_t stream) {
   if (!g_prof.on || g_prof.marks.size() % 2 == 0) return;
   hipEvent_t e = prof_event();
@@ -91,6 +95,22 @@ extern "C" {
 gqa_status gqa_profile_start(void) {
   g_prof.on = true;
   g_prof.marks.clear();
+  g_prof.last_mhz = 0.0;
+  // the clock accumulator is optional: without it only the times are kept
+  int dev = -1;
+  if (hipGetDevice(&dev) == hipSuccess) {
+    if (g_prof.clk && g_prof.clk_device != dev) {
+      (void)hipFree(g_prof.clk);
+      g_prof.clk = nullptr;
+    }
+    if (!g_prof.clk && hipMalloc((void**)&g_prof.clk, 2 * sizeof(unsigned long long)) == hipSuccess)
+      g_prof.clk_device = dev;
+    if (g_prof.clk && hipMemset(g_prof.clk, 0, 2 * sizeof(unsigned long long)) != hipSuccess) {
+      (void)hipFree(g_prof.clk);
+      g_prof.clk = nullptr;
+    }
+  }
+  (void)hipGetLastError();  // a failure above leaves no error behind
   return GQA_OK;
 }
 
@@ -109,8 +129,22 @@ gqa_status gqa_profile_stop(double* total_ms, int32_t* count) {
     ++n;
   }
   g_prof.marks.clear();
+  if (g_prof.clk) {
+    unsigned long long c[2] = {0, 0};
+    int khz = 0;
+    if (hipMemcpy(c, g_prof.clk, sizeof(c), hipMemcpyDeviceToHost) == hipSuccess && c[1] > 0 &&
+        hipDeviceGetAttribute(&khz, hipDeviceAttributeWallClockRate, g_prof.clk_device) == hipSuccess && khz > 0)
+      g_prof.last_mhz = (double)c[0] / (double)c[1] * (double)khz * 1e-3;
+    (void)hipGetLastError();
+  }
   *total_ms = sum;
   *count = n;
+  return GQA_OK;
+}
+
+gqa_status gqa_profile_clock_mhz(double* mhz) {
+  if (!mhz) return GQA_ERR_INVALID;
+  *mhz = g_prof.last_mhz;
   return GQA_OK;
 }
 

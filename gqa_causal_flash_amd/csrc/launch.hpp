@@ -13,6 +13,9 @@ namespace gqa {
 // attention kernel with these; both are no-ops unless profiling is on.
 void prof_before(hipStream_t stream);
 void prof_after(hipStream_t stream);
+// Device accumulator {shader clock cycles, wall-clock ticks} that the prefill
+// kernel adds its workgroups' lifetimes to while profiling is on, else null.
+unsigned long long* prof_clock();
 
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* o, int nq, int n_kv, int q_pos0,
                                  int hq, float scale, void* workspace, hipStream_t stream);

@@ -48,6 +48,7 @@ struct PrefillParams {
   int nqb;
   int grid;
   int split;  // key-split pieces per q-block (0: stream-K split)
+  unsigned long long* clk;  // profiling: {shader cycles, wall ticks} accumulator, or null
   uint32_t part_bytes;
   float c;  // scale * log2(e): scores are kept in log2 units
 };
@@ -401,8 +402,7 @@ __device__ __forceinline__ void prefill_run(const PrefillParams& p, char* smem, 
 }
 
 template <int C, int W>
-__global__ __launch_bounds__(64 * W, (C == 1 && W == 4 ? 2 : 1)) void prefill_causal_fwd(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[(C == 1 && W == 4) ? 2 * kTileBytes : 4 * kTileBytes];
+__device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, char* smem) {
   const int w = blockIdx.x;
   if (p.split > 0) {
     // q-blocks are dispatched last first: they are the longest, so the
@@ -433,6 +433,28 @@ __global__ __launch_bounds__(64 * W, (C == 1 && W == 4 ? 2 : 1)) void prefill_ca
     t0 = seg_end;
     cb += nt;
     ++b;
+  }
+}
+
+template <int C, int W>
+__global__ __launch_bounds__(64 * W, (C == 1 && W == 4 ? 2 : 1)) void prefill_causal_fwd(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[(C == 1 && W == 4) ? 2 * kTileBytes : 4 * kTileBytes];
+  // profiling only: the workgroup's lifetime in shader cycles and wall ticks
+  // as seen by its first wave (clock64: shader clock; wall_clock64: constant
+  // rate); lane 0 adds them to the accumulator with vector atomics
+  const bool stamp = p.clk != nullptr && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  unsigned long long c0 = 0, r0 = 0;
+  if (stamp) {
+    c0 = clock64();
+    r0 = wall_clock64();
+  }
+  prefill_workgroup<C, W>(p, smem);
+  if (stamp) {
+    const unsigned long long dc = clock64() - c0, dr = wall_clock64() - r0;
+    if (threadIdx.x == 0) {
+      atomicAdd(p.clk, dc);
+      atomicAdd(p.clk + 1, dr);
+    }
   }
 }
 
@@ -515,6 +537,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.split = s.split;
   p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
   p.c = scale * kLog2e;
+  p.clk = prof_clock();
   prof_before(stream);
   hipLaunchKernelGGL((prefill_causal_fwd<kPrefillC, kPrefillW>), dim3(s.grid), dim3(64 * kPrefillW), 0, stream, p);
   hipError_t e = hipGetLastError();

@@ -144,3 +144,10 @@ def test_verify_rejects_before_launch(kw, status):
 def test_paged_dropped_rejects_null():
     n = ctypes.c_int32()
     assert g.lib().gqa_prefill_paged_sparse_dropped(None, ctypes.byref(n), None) == g.GQA_ERR_INVALID
+
+
+def test_profile_clock_before_any_session_is_zero():
+    mhz = ctypes.c_double(-1.0)
+    assert g.lib().gqa_profile_clock_mhz(ctypes.byref(mhz)) == g.GQA_OK
+    assert mhz.value == 0.0
+    assert g.lib().gqa_profile_clock_mhz(None) == g.GQA_ERR_INVALID

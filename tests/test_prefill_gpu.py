@@ -70,3 +70,19 @@ def test_prefill_full_size_sampled_rows(cfg):
                                      rng.choice(cfg.nq, 57, replace=False)]))
     ref, _ = oracle.prefill_causal(q, k, v, cfg.q_pos0, SCALE, rows=rows)
     assert_parity(out[rows], ref, cfg.name)
+
+
+def test_prefill_profiling_times_and_clock():
+    """Profiling brackets the main kernel and samples the shader clock; results are unchanged."""
+    import gqa_causal_flash_amd as g
+
+    nq, n_kv = 512, 9000
+    q, k, v = workloads.causal_inputs(nq, n_kv, seed=9)
+    plain = _gpu(q, k, v, n_kv - nq)
+    g.gqa_profile_start()
+    profiled = _gpu(q, k, v, n_kv - nq)
+    ms, n = g.gqa_profile_stop()
+    mhz = g.gqa_profile_clock_mhz()
+    assert np.array_equal(plain, profiled)
+    assert n == 1 and ms > 0
+    assert 300.0 < mhz < 3000.0, mhz
