@@ -9,7 +9,7 @@
 // selection.
 //
 // Two kernels:
-//   paged_prepass  one workgroup per query block: bounds-checks each block id
+//   paged_prepass  one workgroup of 512 threads per query block: bounds-checks each block id
 //                  and page, maps block x to its first physical cache row
 //                  page_table[x/4]*16 + 4*(x%4) (a 4-token block never
 //                  straddles a 16-token page), marks stale and invalid
@@ -37,6 +37,7 @@ namespace gqa {
 namespace {
 
 constexpr int kWaves = 4;
+constexpr int kPrepassThreads = 512;  // sort lanes of the prepass (one workgroup per query block)
 constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // buffer offset past any cache: reads zeros
 
 struct PagedParams {
@@ -56,7 +57,7 @@ struct PagedParams {
 };
 
 // ------------------------------------------------------------------ prepass
-__global__ __launch_bounds__(256) void paged_prepass(PagedParams p) {
+__global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) {
   __shared__ unsigned long long keys[kSortMax];
   __shared__ int errs;
   const int b = blockIdx.x;
@@ -110,13 +111,13 @@ __global__ __launch_bounds__(256) void paged_prepass(PagedParams p) {
     int npow = 1;
     while (npow < n) npow <<= 1;
     int bad = 0;
-    for (int i = tid; i < npow; i += 256) keys[i] = (i < n) ? translate(i, bad) : ~0ull;
+    for (int i = tid; i < npow; i += kPrepassThreads) keys[i] = (i < n) ? translate(i, bad) : ~0ull;
     if (bad) atomicAdd(&errs, bad);
     __syncthreads();
     // bitonic sort, ascending
     for (int k = 2; k <= npow; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < npow; i += 256) {
+        for (int i = tid; i < npow; i += kPrepassThreads) {
           const int ixj = i ^ j;
           if (ixj > i) {
             const unsigned long long a = keys[i], c = keys[ixj];
@@ -132,7 +133,7 @@ __global__ __launch_bounds__(256) void paged_prepass(PagedParams p) {
     }
     // drop duplicates (same physical row) and count the valid prefix
     int dup = 0, valid = 0;
-    for (int i = tid; i < n; i += 256) {
+    for (int i = tid; i < n; i += kPrepassThreads) {
       unsigned long long kv = keys[i];
       if (kv != ~0ull && i > 0 && (keys[i - 1] >> 32) == (kv >> 32)) {
         kv = ~0ull;
@@ -155,7 +156,7 @@ __global__ __launch_bounds__(256) void paged_prepass(PagedParams p) {
   } else {
     // too long to sort in LDS: keep the given order (it is only a locality choice)
     int bad = 0;
-    for (int i = tid; i < n; i += 256) {
+    for (int i = tid; i < n; i += kPrepassThreads) {
       const unsigned long long kv = translate(i, bad);
       ent[start + i] = (kv == ~0ull) ? int2{-1, 0x7FFFFFFF} : int2{(int)(kv >> 32), (int)(kv & 0xFFFFFFFFu)};
     }
@@ -385,7 +386,7 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   p.part_bytes = (uint32_t)(L.total - L.part);
   p.pieces = L.pieces;
   p.c = scale * kLog2e;
-  hipLaunchKernelGGL(paged_prepass, dim3(p.nqb), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(paged_prepass, dim3(p.nqb), dim3(kPrepassThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // ids are grouped by XCD (see paged_unit): round the query blocks up to a multiple of 8
