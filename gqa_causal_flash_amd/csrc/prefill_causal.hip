@@ -15,7 +15,7 @@
 // (16 steps of 16 head-dim columns) and its O^T accumulator (8 tiles of 32x32
 // fp32).  K/V tiles of 64 keys stream HBM -> LDS by direct-to-LDS loads into a
 // double buffer (2 x 64 KiB).  (Templates C and W give other row splits,
-// 32C rows per wave and W waves, kept for measurement.)
+// 32C rows per wave and W waves; the default is C = 1, W = 8.)
 #include "attn_common.hpp"
 #include "attn_tile.hpp"
 #include "prefill_sched.hpp"
@@ -199,206 +199,10 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
   }
 }
 
-// Phase-shifted variant of prefill_piece for 8 waves of 32 rows.  Keys are
-// handled in 32-key sub-tiles held in a 4-deep LDS ring (V sub-tiles at 0, 16,
-// 32, 48 KiB; K at 64 .. 112 KiB).  In phase ph, waves 0-3 run
-// scores/softmax/PV of sub-tile ph, while waves 4-7 (one per SIMD as well)
-// run softmax/PV of sub-tile ph-1 and then the scores of sub-tile ph.  The two
-// waves of a SIMD are therefore in different parts of the step at any time:
-// the softmax arithmetic of one overlaps the matrix-core work of the other.
-// Sub-tile ph+2 is loaded during phase ph (into the slot sub-tile ph-2 used),
-// and each wave's loads of sub-tile ph+1 are complete before the barrier that
-// ends phase ph.
-__device__ __forceinline__ void wait_vmem_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
-
-__device__ __forceinline__ void prefill_piece_pingpong(const PrefillParams& p, char* smem, int b, int tile_lo,
-                                                       int tile_hi, bool full, int slot) {
-  constexpr int W = 8;
-  constexpr int kSub = 32;
-  constexpr int kSubBytes = kSub * kRowBytes;  // 16 KiB per K or V sub-tile
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int trail = wave >> 2;  // 0: waves 0-3, 1: waves 4-7
-  const int half = lane >> 5;
-  const int col = lane & 31;
-  const uint32_t kl = 512u * half + 16u * (uint32_t)(col ^ half);
-  const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
-
-  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
-  const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes);
-  const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes);
-
-  const int row_base = b * kRowsPerBlock + wave * 32;
-  const bool wave_active = row_base < p.nrows;
-  const int wrow_hi = min(row_base + 31, p.nrows - 1);
-  const int wpos_lo = p.q_pos0 + row_base / kGroup;
-  const int wpos_hi = p.q_pos0 + wrow_hi / kGroup;
-
-  int pos[1];
-  h8 qf[1][16];
-  {
-    const int row = row_base + col;
-    pos[0] = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
-    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
-  }
-  f16x acc[1][8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
-  float m[1] = {-INFINITY}, l[1] = {0.f};
-  uint32_t bk = k_lane_base(lane);
-  uint32_t bv = v_lane_base(lane);
-
-  const int n_sub = 2 * (tile_hi - tile_lo);
-  const int key_base = tile_lo * kTileKeys;
-  auto issue_sub = [&](int x) {
-    const int buf = x & 3;
-    issue_rows<W, kSub>(rk, rv, (uint32_t)(key_base + kSub * x) * kRowBytes, smem + (4 + buf) * kSubBytes,
-                        smem + buf * kSubBytes, wave, kl, vl);
-  };
-  auto visible_at = [&](int k0) { return [=](int c, int vv) { return k0 + lane_key(vv, half) <= pos[c]; }; };
-
-  if (n_sub > 0) issue_sub(0);
-  if (n_sub > 1) issue_sub(1);
-  wait_vmem();
-  __syncthreads();
-
-  // One code path for both groups: leaders compute the scores of sub-tile ph
-  // first, trailers last (carrying them into the next phase).
-  f16x sc[1];
-  int x = -1;  // sub-tile whose scores are in sc, -1 if none
-  auto scores = [&](int ph) {
-    const int k0 = key_base + kSub * ph;
-    if (ph < n_sub && wave_active && k0 <= wpos_hi) {
-      qk_32keys<1>(lds_addr((const GQA_LDS char*)smem + (4 + (ph & 3)) * kSubBytes) + bk, 0, qf, sc);
-      x = ph;
-    }
-  };
-  for (int ph = 0; ph <= n_sub; ++ph) {
-    const bool load = ph + 2 < n_sub;
-    if (load) issue_sub(ph + 2);
-    asm volatile("" : "+v"(bk), "+v"(bv));
-    if (trail == 0) scores(ph);
-    if (x >= 0) {
-      const int k0 = key_base + kSub * x;
-      h8 pk[1][2];
-      softmax_32keys<1>(sc, acc, m, l, p.c, k0 + 31 > wpos_lo, visible_at(k0), pk);
-      pv_32keys<1>((const GQA_LDS char*)smem + (x & 3) * kSubBytes, bv, 0, pk, acc);
-      x = -1;
-    }
-    if (trail == 1) scores(ph);
-    if (load)
-      wait_vmem_4();  // this phase's 4 copies may stay in flight; sub-tile ph+1 has landed
-    else
-      wait_vmem();
-    __syncthreads();
-  }
-
-  const float lt = swap_halves_sum(l[0]);
-  if (full) {
-    const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-    store_rows_f16(ro, row_base + col, half, acc[0], lt, 1.0f);
-  } else {
-    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-    const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
-    store_partial(rp, sbase, kRowsPerBlock, wave * 32 + col, half, acc[0], m[0], lt);
-  }
-}
-
-// Variant for 4 waves of 32 rows (128-row q-blocks, two workgroups per
-// compute unit): keys in 32-key sub-tiles through a 2-deep LDS ring (V at 0
-// and 16 KiB, K at 32 and 48 KiB).  The two waves that share a SIMD belong to
-// different workgroups, so their barriers are independent and one computes
-// while the other waits.
-__device__ __forceinline__ void prefill_piece_ring(const PrefillParams& p, char* smem, int b, int tile_lo,
-                                                   int tile_hi, bool full, int slot) {
-  constexpr int W = 4;
-  constexpr int kSub = 32;
-  constexpr int kSubBytes = kSub * kRowBytes;  // 16 KiB
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int half = lane >> 5;
-  const int col = lane & 31;
-  const uint32_t kl = 512u * half + 16u * (uint32_t)(col ^ half);
-  const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
-
-  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
-  const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes);
-  const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes);
-
-  const int row_base = b * kRowsPerBlock + wave * 32;
-  const bool wave_active = row_base < p.nrows;
-  const int wrow_hi = min(row_base + 31, p.nrows - 1);
-  const int wpos_lo = p.q_pos0 + row_base / kGroup;
-  const int wpos_hi = p.q_pos0 + wrow_hi / kGroup;
-
-  int pos[1];
-  h8 qf[1][16];
-  {
-    const int row = row_base + col;
-    pos[0] = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
-    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
-  }
-  f16x acc[1][8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
-  float m[1] = {-INFINITY}, l[1] = {0.f};
-  uint32_t bk = k_lane_base(lane);
-  uint32_t bv = v_lane_base(lane);
-
-  const int n_sub = 2 * (tile_hi - tile_lo);
-  const int key_base = tile_lo * kTileKeys;
-  auto issue_sub = [&](int x) {
-    const int buf = x & 1;
-    issue_rows<W, kSub>(rk, rv, (uint32_t)(key_base + kSub * x) * kRowBytes, smem + (2 + buf) * kSubBytes,
-                        smem + buf * kSubBytes, wave, kl, vl);
-  };
-  if (n_sub > 0) issue_sub(0);
-  wait_vmem();
-  __syncthreads();
-  for (int ph = 0; ph < n_sub; ++ph) {
-    if (ph + 1 < n_sub) issue_sub(ph + 1);
-    asm volatile("" : "+v"(bk), "+v"(bv));
-    const int k0 = key_base + kSub * ph;
-    if (wave_active && k0 <= wpos_hi) {
-      const int buf = ph & 1;
-      attend_32keys<1>(lds_addr((const GQA_LDS char*)smem + (2 + buf) * kSubBytes) + bk,
-                       (const GQA_LDS char*)smem + buf * kSubBytes, bv, 0, qf, acc, m, l, p.c, k0 + 31 > wpos_lo,
-                       [&](int c, int vv) { return k0 + lane_key(vv, half) <= pos[c]; });
-    }
-    wait_vmem();
-    __syncthreads();
-  }
-
-  const float lt = swap_halves_sum(l[0]);
-  if (full) {
-    const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-    store_rows_f16(ro, row_base + col, half, acc[0], lt, 1.0f);
-  } else {
-    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-    const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
-    store_partial(rp, sbase, kRowsPerBlock, wave * 32 + col, half, acc[0], m[0], lt);
-  }
-}
-
-#ifndef GQA_PREFILL_PINGPONG
-#define GQA_PREFILL_PINGPONG 0
-#endif
-
 template <int C, int W>
 __device__ __forceinline__ void prefill_run(const PrefillParams& p, char* smem, int b, int lo, int hi, bool full,
                                             int slot) {
-  if constexpr (C == 1 && W == 4)
-    prefill_piece_ring(p, smem, b, lo, hi, full, slot);
-  else if constexpr (GQA_PREFILL_PINGPONG && C == 1 && W == 8)
-    prefill_piece_pingpong(p, smem, b, lo, hi, full, slot);
-  else
-    prefill_piece<C, W>(p, smem, b, lo, hi, full, slot);
+  prefill_piece<C, W>(p, smem, b, lo, hi, full, slot);
 }
 
 template <int C, int W>
@@ -437,8 +241,8 @@ __device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, char* 
 }
 
 template <int C, int W>
-__global__ __launch_bounds__(64 * W, (C == 1 && W == 4 ? 2 : 1)) void prefill_causal_fwd(PrefillParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[(C == 1 && W == 4) ? 2 * kTileBytes : 4 * kTileBytes];
+__global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
   // profiling only: the workgroup's lifetime in shader cycles and wall ticks
   // as seen by its first wave (clock64: shader clock; wall_clock64: constant
   // rate); lane 0 adds them to the accumulator with vector atomics

@@ -26,9 +26,8 @@ namespace gqa {
 #ifndef GQA_PREFILL_ROWS
 #define GQA_PREFILL_ROWS 256
 #endif
-constexpr int kRowsPerBlock = GQA_PREFILL_ROWS;  // packed rows per workgroup (256: 8 waves, 128: 4 waves)
-// workgroups resident per compute unit (LDS: 128 KiB for 256 rows, 64 KiB for 128 rows)
-constexpr int kWGsPerCU = kRowsPerBlock == 256 ? 1 : 2;
+constexpr int kRowsPerBlock = GQA_PREFILL_ROWS;  // packed rows per workgroup
+constexpr int kWGsPerCU = 1;                     // 128 KiB of LDS per workgroup
 constexpr int kTileKeys = 64;       // keys per K/V tile
 constexpr int kTargetGrid = 256;    // one workgroup per MI355X compute unit
 constexpr int kMinTilesPerWG = 16;

@@ -37,3 +37,23 @@ def test_verify_parity_edges(nq, ctx):
 def test_verify_deterministic():
     x = workloads.verify_inputs(8, 50000, seed=3)
     assert np.array_equal(_gpu(x), _gpu(x))
+
+
+def test_verify_decodes_every_e4m3_code_exactly():
+    """One query row, one key: O equals the decoded V row, so all 256 codes (one per
+    head-dim column) must come back as their exact values, NaN for 0x7F and 0xFF."""
+    import gqa_causal_flash_amd as g
+
+    rng = np.random.default_rng(11)
+    q = rng.standard_normal((1, 6, 256)).astype(np.float16)
+    kb = np.zeros((1, 1, 256), dtype=np.uint8)  # code 0 = +0: a finite score
+    vb = np.arange(256, dtype=np.uint8).reshape(1, 1, 256)
+    out = to_host(g.gqa_verify_fp8kv(to_dev(q), to_dev(kb), to_dev(vb), 1.0, 1.0, workloads.SCALE))
+    want = oracle.e4m3_decode(vb[0, 0]).astype(np.float16)  # every E4M3 value is exact in fp16
+    for h in range(6):
+        got = out[0, h]
+        nan = np.isnan(want)
+        assert np.array_equal(np.isnan(got), nan), h
+        # exact values (code 0x80, -0, comes back as +0: the accumulator starts at +0)
+        assert np.array_equal(got[~nan], want[~nan]), h
+    assert nan.sum() == 2 and nan[0x7F] and nan[0xFF]
