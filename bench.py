@@ -17,8 +17,10 @@ Prints ONE JSON line.  Besides the driver's fields it carries
                 fraction of the peak rescaled to that clock;
   cpu_baseline  the fp64 oracle timed on this host's cores for a bounded sample
                 of query rows of the same workload, in the same unit;
-  paths         the same measurement for the other entry points (paged
-                block-sparse prefill, FP8 verifier tail) when they are built.
+  paths         the same measurement for the other entry points: the paged
+                block-sparse prefill (S = 64/512/2048), the paged dense causal
+                prefill (every block selected, pages of 16 and 784 tokens) and
+                the FP8 verifier tail (q = 2/4/8).
 
 `roofline.traffic` is the HBM traffic per launch of that kernel, read from the
 committed counter summary (profiles/hbm_traffic_per_launch.md) when the kernel
@@ -58,6 +60,7 @@ PAGE_MS_Q8000_KV128000 = 100.20284
 
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_per_launch.md")
 PAGED_SELECTIONS = (64, 512, 2048)
+PAGED_DENSE_PAGES = (16, 784)  # paged dense causal prefill: every block up to the diagonal selected
 VERIFY_QUERIES = (2, 4, 8)
 
 
@@ -67,6 +70,10 @@ def prefill_workload(n_kv: int) -> str:
 
 def paged_workload(select_tokens: int, tail: int = 1) -> str:
     return f"paged_sparse_q4096_page16_select{select_tokens}_tail{tail}"
+
+
+def paged_dense_workload(page_size: int, tail: int = 1) -> str:
+    return f"paged_dense_causal_q4096_page{page_size}_tail{tail}"
 
 
 def verify_workload(nq: int) -> str:
@@ -129,7 +136,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
     per = warmup + steps
     first = {"prefill_causal_fwd": "prefill", "paged_prepass": "paged", "verify_fwd": "verify"}
     labels = {"prefill": [prefill_workload(n_kv)],
-              "paged": [paged_workload(s) for s in PAGED_SELECTIONS],
+              "paged": [paged_workload(s) for s in PAGED_SELECTIONS] + [paged_dense_workload(p) for p in PAGED_DENSE_PAGES],
               "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
     true_kib = calib_mib * 1024.0
     result, factors = {}, {}
@@ -270,12 +277,20 @@ def paged_visible_pairs(x) -> int:
     return total
 
 
-def bench_paged(select_tokens, steps, warmup, tail=1, seed=0):
+def bench_paged(select_tokens, steps, warmup, tail=1, seed=0, dense_page_size=None):
+    """Paged block-sparse prefill with S-token selections, or (dense_page_size set) the paged
+    dense causal prefill with every block up to the diagonal selected over pages of that size."""
     import torch
 
     import gqa_causal_flash_amd as g
 
-    x = workloads.paged_sparse_inputs(select_tokens=select_tokens, tail=tail, seed=seed)
+    if dense_page_size is None:
+        x = workloads.paged_sparse_inputs(select_tokens=select_tokens, tail=tail, seed=seed)
+        name = paged_workload(select_tokens, tail)
+    else:
+        x = workloads.paged_sparse_inputs(select_tokens=4, tail=tail, seed=seed, saturate=True,
+                                          page_size=dense_page_size)
+        name = paged_dense_workload(dense_page_size, tail)
     dev = {k: torch.from_numpy(np.ascontiguousarray(getattr(x, k))).cuda()
            for k in ("q", "k_cache", "v_cache", "page_table", "qblock_offsets", "kv_block_ids")}
     o = torch.empty_like(dev["q"])
@@ -294,16 +309,18 @@ def bench_paged(select_tokens, steps, warmup, tail=1, seed=0):
     gathered = sum(max(0, int(min(x.live_len, 4 * (b + 1)) - 4 * b)) for b in x.kv_block_ids) * 2 * 512
     moved = gathered + 2 * x.q.nbytes
     tf = flops / (kms * 1e-3) / 1e12
-    return {
-        "workload": paged_workload(select_tokens, tail),
+    line = {
+        "workload": name,
         "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "visible_pairs_per_head": pairs,
         "roofline": {"kernel": "paged_fwd", "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 4),
                      "moved_GBps": round(moved / (kms * 1e-3) / 1e9, 1),
-                     "traffic": recorded_traffic().get(("paged_fwd", paged_workload(select_tokens, tail)))},
-        "page_ms_v100": {64: 1.010, 512: 3.204, 2048: 11.203}[select_tokens],
+                     "traffic": recorded_traffic().get(("paged_fwd", name))},
     }
+    if dense_page_size is None:
+        line["page_ms_v100"] = {64: 1.010, 512: 3.204, 2048: 11.203}[select_tokens]
+    return line
 
 
 def bench_verify(nq, steps, warmup, copies=3, seed=0):
@@ -420,6 +437,7 @@ def main(argv=None):
     if not args.no_paths:
         line["paths"] = {
             "paged_sparse": [bench_paged(sel, args.steps, args.warmup) for sel in PAGED_SELECTIONS],
+            "paged_dense": [bench_paged(None, args.steps, args.warmup, dense_page_size=ps) for ps in PAGED_DENSE_PAGES],
             "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in VERIFY_QUERIES],
         }
     if not args.no_cpu_baseline:

@@ -227,12 +227,12 @@ gqa_status gqa_prefill_paged_sparse(const void* q, const void* k_cache, const vo
   gqa_status st = gqa_prefill_paged_sparse_workspace_size(nq, n_block_ids, qblock_rows, kv_block_tokens, hq, hkv, d,
                                                           &need);
   if (st != GQA_OK) return st;
-  if (page_size != gqa::kPageSize) return GQA_ERR_UNSUPPORTED;
+  if (page_size % gqa::kBlockTokens != 0 || page_size > gqa::kMaxPageSize) return GQA_ERR_UNSUPPORTED;
   if ((int64_t)q_pos0 + nq > live_len || (int64_t)live_len > (int64_t)n_table * page_size) return GQA_ERR_INVALID;
   // the cache buffer plus the out-of-range marker offset must fit 32 bits
   if ((int64_t)n_pages * page_size * hkv * d * 2 > 0xFFFFFF00ll) return GQA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
-  return hip_status(gqa::launch_paged_sparse(q, k_cache, v_cache, page_table, n_table, n_pages, qblock_offsets,
+  return hip_status(gqa::launch_paged_sparse(q, k_cache, v_cache, page_table, n_table, n_pages, page_size, qblock_offsets,
                                              kv_block_ids, n_block_ids, nq, q_pos0, live_len, hq, scale, o, workspace,
                                              (hipStream_t)stream));
 }

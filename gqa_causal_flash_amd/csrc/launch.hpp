@@ -21,7 +21,8 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
                                  int hq, float scale, void* workspace, hipStream_t stream);
 
 hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
-                               int n_table, int n_pages, const int32_t* qblock_offsets, const int32_t* kv_block_ids,
+                               int n_table, int n_pages, int page_size, const int32_t* qblock_offsets,
+                               const int32_t* kv_block_ids,
                                int n_block_ids, int nq, int q_pos0, int live_len, int hq, float scale, void* o,
                                void* workspace, hipStream_t stream);
 

@@ -19,8 +19,8 @@
 
 namespace gqa {
 
-constexpr int kPageSize = 16;
 constexpr int kBlockTokens = 4;
+constexpr int kMaxPageSize = 4096;  // tokens per page; any multiple of kBlockTokens up to this
 constexpr int kQBlockTokens = 64;
 constexpr int kQBlockRows = kQBlockTokens * 6;  // 384 packed rows
 constexpr int kPagedRowsPerWG = 128;

@@ -11,8 +11,9 @@
 // Two kernels:
 //   paged_prepass  one workgroup of 512 threads per query block: bounds-checks each block id
 //                  and page, maps block x to its first physical cache row
-//                  page_table[x/4]*16 + 4*(x%4) (a 4-token block never
-//                  straddles a 16-token page), marks stale and invalid
+//                  page_table[x/(P/4)]*P + 4*(x%(P/4)) for pages of P tokens
+//                  (P a multiple of 4, so a 4-token block never straddles a
+//                  page: 16 and 784 in the pages' geometries), marks stale and invalid
 //                  blocks, sorts the list by physical row and drops
 //                  duplicates.
 //   paged_fwd      three workgroups per query block (128 packed rows each):
@@ -49,7 +50,7 @@ struct PagedParams {
   const int32_t* ids;
   _Float16* o;
   char* ws;
-  int n_table, n_pages, n_ids, nq, nrows, nqb, q_pos0, live_len;
+  int n_table, n_pages, page_size, n_ids, nq, nrows, nqb, q_pos0, live_len;
   size_t off_err, off_beg, off_cnt, off_entries, off_part;
   uint32_t part_bytes;
   int pieces;
@@ -86,7 +87,8 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
   int bad_range = (o0 < 0 || o0 > p.n_ids || o1 < 0 || o1 > p.n_ids || o1 < o0) ? 1 : 0;
   if (end < start) end = start;
   const int n = end - start;
-  const int n_blocks_table = p.n_table * (kPageSize / kBlockTokens);
+  const int blocks_per_page = p.page_size / kBlockTokens;
+  const int n_blocks_table = p.n_table * blocks_per_page;
 
   // Translate entry i of this block: valid -> (physical row << 32 | token),
   // otherwise all ones (sorts last).
@@ -98,12 +100,12 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     }
     const int tok0 = x * kBlockTokens;
     if (tok0 >= p.live_len) return ~0ull;  // stale block: not an error, just nothing live
-    const int page = (int)__builtin_amdgcn_raw_buffer_load_b32(rpt, (uint32_t)(x / (kPageSize / kBlockTokens)) * 4, 0, 0);
+    const int page = (int)__builtin_amdgcn_raw_buffer_load_b32(rpt, (uint32_t)(x / blocks_per_page) * 4, 0, 0);
     if (page < 0 || page >= p.n_pages) {
       bad = 1;
       return ~0ull;
     }
-    const unsigned row = (unsigned)page * kPageSize + (unsigned)(x % (kPageSize / kBlockTokens)) * kBlockTokens;
+    const unsigned row = (unsigned)page * (unsigned)p.page_size + (unsigned)(x % blocks_per_page) * kBlockTokens;
     return ((unsigned long long)row << 32) | (unsigned)tok0;
   };
 
@@ -244,7 +246,7 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   const int s_hi = (int)((long long)(pj + 1) * n_sub / p.pieces);
 
   const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
-  const uint32_t cache_bytes = (uint32_t)p.n_pages * kPageSize * kRowBytes;
+  const uint32_t cache_bytes = (uint32_t)p.n_pages * (uint32_t)p.page_size * kRowBytes;
   const rsrc_t rk = make_rsrc(p.kc, cache_bytes);
   const rsrc_t rv = make_rsrc(p.vc, cache_bytes);
 
@@ -357,7 +359,8 @@ __global__ __launch_bounds__(256) void paged_merge(PagedParams p) {
 }  // namespace
 
 hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v_cache, const int32_t* page_table,
-                               int n_table, int n_pages, const int32_t* qblock_offsets, const int32_t* kv_block_ids,
+                               int n_table, int n_pages, int page_size, const int32_t* qblock_offsets,
+                               const int32_t* kv_block_ids,
                                int n_block_ids, int nq, int q_pos0, int live_len, int hq, float scale, void* o,
                                void* workspace, hipStream_t stream) {
   PagedParams p;
@@ -371,6 +374,7 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   p.ws = (char*)workspace;
   p.n_table = n_table;
   p.n_pages = n_pages;
+  p.page_size = page_size;
   p.n_ids = n_block_ids;
   p.nq = nq;
   p.nrows = nq * hq;

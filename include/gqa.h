@@ -88,7 +88,10 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
  * main", Changes): selected four-token blocks of a paged page-16 cache are
  * fetched in locality order for the Hq6/Hkv1/D256 prefill, positions are
  * clamped to the live request length and a partial tail block is admitted
- * only for the tokens that exist.
+ * only for the tokens that exist.  Selecting every block up to the diagonal
+ * gives the paged dense causal prefill of the same page (Test Result: the
+ * page-16 and page-784 smokes), so any page size that is a multiple of the
+ * 4-token block is accepted.
  *
  *   q        [nq][hq][d] fp16, query row r at position q_pos0 + r
  *   k_cache, v_cache [n_pages][page_size][hkv][d] fp16
@@ -105,7 +108,8 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
  *   Row r of block b sees token j iff j lies in a selected block of b,
  *   j <= q_pos0 + r and j < live_len.  A row that sees nothing outputs 0.
  *   requires q_pos0 >= 0, q_pos0 + nq <= live_len <= n_table * page_size;
- *   this version requires page_size = 16, kv_block_tokens = 4,
+ *   this version requires page_size to be a multiple of 4 up to 4096
+ *   (16 and 784 in the page's geometries), kv_block_tokens = 4 and
  *   qblock_rows = 64 (GQA_ERR_UNSUPPORTED otherwise).
  *
  *   The index arrays live in device memory and are checked on the device,

@@ -99,7 +99,10 @@ def _paged(**kw):
     (dict(live_len=4096), g.GQA_ERR_INVALID),       # q_pos0 + nq > live_len
     (dict(live_len=257 * 16 + 1), g.GQA_ERR_INVALID),  # live tokens beyond the table
     (dict(n_pages=0), g.GQA_ERR_INVALID),
-    (dict(page_size=32), g.GQA_ERR_UNSUPPORTED),
+    (dict(page_size=30), g.GQA_ERR_UNSUPPORTED),    # pages must hold whole 4-token blocks
+    (dict(page_size=8192, n_pages=2), g.GQA_ERR_UNSUPPORTED),
+    (dict(page_size=784, n_table=6, n_pages=12), g.GQA_ERR_WORKSPACE),  # the page-784 geometry is accepted
+    (dict(page_size=784, n_table=5, n_pages=12), g.GQA_ERR_INVALID),    # 5 pages of 784 < live_len
     (dict(kbt=8), g.GQA_ERR_UNSUPPORTED),
     (dict(qbr=128), g.GQA_ERR_UNSUPPORTED),
     (dict(hq=8), g.GQA_ERR_UNSUPPORTED),

@@ -85,6 +85,29 @@ def test_paged_saturated_matches_dense_causal():
     assert_parity(out, ref, "saturated")
 
 
+@pytest.mark.parametrize("select,tail", [(64, 0), (512, 1), (2048, 3)])
+def test_paged_page784_parity(select, tail):
+    """The block-sparse selection over a page-784 cache (non-monotonic table of 784-token pages)."""
+    x = workloads.paged_sparse_inputs(select_tokens=select, tail=tail, seed=300 + select + tail, page_size=784)
+    assert x.page_size == 784 and x.k_cache.shape[1] == 784
+    assert_parity(_gpu(x), _oracle(x), f"page 784 S={select} t={tail}")
+
+
+@pytest.mark.parametrize("page_size", [16, 784])
+def test_paged_dense_causal_full_size(page_size):
+    """Paged dense causal prefill (every block up to the diagonal selected), 4096 rows, against
+    dense causal attention over the logical cache."""
+    x = workloads.paged_sparse_inputs(select_tokens=64, tail=1, seed=31, saturate=True, page_size=page_size)
+    out = _gpu(x)
+    from oracle import attention as oatt
+
+    toks = np.arange(x.live_len)
+    kc = oatt.gather_paged(x.k_cache, x.page_table, page_size, toks)
+    vc = oatt.gather_paged(x.v_cache, x.page_table, page_size, toks)
+    ref, _ = oracle.prefill_causal(x.q, kc, vc, x.q_pos0, x.scale)
+    assert_parity(out, ref, f"paged dense page {page_size}")
+
+
 def test_paged_invalid_and_duplicate_entries_are_dropped():
     """Out-of-range block ids, out-of-range pages and duplicates contribute nothing and are counted."""
     import gqa_causal_flash_amd as g

@@ -89,15 +89,16 @@ class PagedSparseInputs:
     meta: dict = field(default_factory=dict)
 
 
-def paged_sparse_inputs(select_tokens: int, tail: int, seed: int, nq: int = 4096, n_pages: int = PAGE_POOL,
+def paged_sparse_inputs(select_tokens: int, tail: int, seed: int, nq: int = 4096, n_pages: int | None = None,
                         poison_stale: bool = False, saturate: bool = False, identity_table: bool = False,
-                        hq: int = HQ, hkv: int = HKV, d: int = D) -> PagedSparseInputs:
+                        page_size: int = PAGE_SIZE, hq: int = HQ, hkv: int = HKV, d: int = D) -> PagedSparseInputs:
     """Paged block-sparse prefill inputs.
 
     Query row r sits at position tail + r, so the request holds ``tail`` tokens
     of earlier context and live_len = tail + nq.  The page table maps the
-    ceil(live_len / 16) logical pages to distinct physical pages drawn as a
-    seeded random permutation of the pool (non-monotonic).  Query block b (rows
+    ceil(live_len / page_size) logical pages to distinct physical pages drawn
+    as a seeded random permutation of the pool (non-monotonic); the pool holds
+    512 pages at page size 16 and twice the pages the request needs otherwise.  Query block b (rows
     64b..64b+63) always selects the 4-token block holding the position of its
     last row (its causal-diagonal block, of which only part may be visible: the
     partial tail), plus min(select_tokens/4 - 1, diag) distinct random earlier
@@ -106,20 +107,24 @@ def paged_sparse_inputs(select_tokens: int, tail: int, seed: int, nq: int = 4096
     """
     if select_tokens % KV_BLOCK_TOKENS or select_tokens < KV_BLOCK_TOKENS:
         raise ValueError("selection must be a positive multiple of the block size")
+    if page_size % KV_BLOCK_TOKENS or page_size <= 0:
+        raise ValueError("page size must be a positive multiple of the block size")
     rng = np.random.default_rng(seed)
-    q = _normal16(rng, (nq, hq, d))
-    k_cache = _normal16(rng, (n_pages, PAGE_SIZE, hkv, d))
-    v_cache = _normal16(rng, (n_pages, PAGE_SIZE, hkv, d))
     live_len = tail + nq
-    n_table = -(-live_len // PAGE_SIZE)
+    n_table = -(-live_len // page_size)
+    if n_pages is None:
+        n_pages = PAGE_POOL if page_size == PAGE_SIZE else 2 * n_table
+    q = _normal16(rng, (nq, hq, d))
+    k_cache = _normal16(rng, (n_pages, page_size, hkv, d))
+    v_cache = _normal16(rng, (n_pages, page_size, hkv, d))
     if n_table > n_pages:
         raise ValueError("page pool too small")
     perm = rng.permutation(n_pages)
     page_table = (np.arange(n_table) if identity_table else perm[:n_table]).astype(np.int32)
     if poison_stale:
-        live = np.zeros((n_pages, PAGE_SIZE), dtype=bool)
+        live = np.zeros((n_pages, page_size), dtype=bool)
         toks = np.arange(live_len)
-        live[page_table[toks // PAGE_SIZE], toks % PAGE_SIZE] = True
+        live[page_table[toks // page_size], toks % page_size] = True
         k_cache[~live] = np.float16(np.nan)
         v_cache[~live] = np.float16(np.nan)
     n_qblocks = -(-nq // QBLOCK_ROWS)
@@ -138,9 +143,9 @@ def paged_sparse_inputs(select_tokens: int, tail: int, seed: int, nq: int = 4096
         q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
         qblock_offsets=np.asarray(offsets, dtype=np.int32),
         kv_block_ids=np.concatenate(ids).astype(np.int32),
-        q_pos0=tail, live_len=live_len,
+        q_pos0=tail, live_len=live_len, page_size=page_size,
         meta=dict(select_tokens=select_tokens, tail=tail, seed=seed, nq=nq, n_pages=n_pages,
-                  poison_stale=poison_stale, saturate=saturate),
+                  poison_stale=poison_stale, saturate=saturate, page_size=page_size),
     )
 
 
