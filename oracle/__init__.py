@@ -18,6 +18,9 @@ heads, head dim D, softmax scale, causal positions):
   the live length clamped away ("[Kernel][SM70] Repair #378 on latest main",
   Changes: four-token block selection, locality-sorted pages, clamp to live
   request length, partial tail admitted only for real tokens).
+* ``prefill_causal_varlen`` -- a batch of independent causal prefills packed
+  end to end (per-sequence offsets), each with its queries at the last
+  positions of its keys.
 * ``verify_fp8kv`` -- a short causal verifier tail (2..8 query rows) over a K/V
   cache stored as OCP E4M3 bytes with one fp32 scale per tensor ("[Perf] Ship
   the qualified SM70 long-context layout...", What / Changes: grouped E4M3 FP32
@@ -34,6 +37,7 @@ from .attention import (
     causal_visible,
     kv_head_of,
     prefill_causal,
+    prefill_causal_varlen,
     prefill_paged_sparse,
     verify_fp8kv,
     visible_pairs_causal,
@@ -45,6 +49,7 @@ __all__ = [
     "causal_visible",
     "kv_head_of",
     "prefill_causal",
+    "prefill_causal_varlen",
     "prefill_paged_sparse",
     "verify_fp8kv",
     "visible_pairs_causal",

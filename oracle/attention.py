@@ -140,6 +140,36 @@ def gather_paged(cache, page_table, page_size: int, tokens: np.ndarray):
     return cache[pages, slots]  # [n_tokens, Hkv, D]
 
 
+def prefill_causal_varlen(q, k, v, cu_q, cu_kv, scale: float):
+    """Causal prefill of a batch of independent sequences packed end to end.
+
+    Sequence i owns query rows cu_q[i] .. cu_q[i+1]-1 of q [total_q, Hq, D]
+    and key rows cu_kv[i] .. cu_kv[i+1]-1 of k, v [total_kv, Hkv, D]; its
+    nq_i queries are the last nq_i positions of its nkv_i keys (the causal
+    convention of the dense prefill, applied per sequence; a serving engine
+    batches requests this way, and the per-row lse lets a caller merge the
+    result with other attention pieces).  Each sequence is exactly
+    ``prefill_causal`` on its own slices, with q_pos0 = nkv_i - nq_i.
+    Returns (o [total_q, Hq, D], lse [total_q, Hq]) in float64.
+    """
+    cu_q = np.asarray(cu_q, dtype=np.int64)
+    cu_kv = np.asarray(cu_kv, dtype=np.int64)
+    total_q, hq, d = q.shape
+    o = np.zeros((total_q, hq, v.shape[2]), dtype=np.float64)
+    lse = np.full((total_q, hq), -np.inf, dtype=np.float64)
+    for i in range(cu_q.size - 1):
+        q0, q1, k0, k1 = cu_q[i], cu_q[i + 1], cu_kv[i], cu_kv[i + 1]
+        nq, nkv = q1 - q0, k1 - k0
+        if nq == 0:
+            continue
+        if nq > nkv:
+            raise ValueError("a sequence has more queries than keys")
+        oi, li = prefill_causal(q[q0:q1], k[k0:k1], v[k0:k1], int(nkv - nq), scale)
+        o[q0:q1] = oi
+        lse[q0:q1] = li
+    return o, lse
+
+
 def prefill_paged_sparse(q, k_cache, v_cache, page_table, page_size: int, qblock_offsets, kv_block_ids,
                          qblock_rows: int, kv_block_tokens: int, q_pos0: int, live_len: int, scale: float):
     """Block-sparse causal GQA prefill over a paged K/V cache.

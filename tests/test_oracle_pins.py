@@ -369,6 +369,56 @@ def test_verify_generator_scale_is_amax_over_448():
     assert x.k_scale > 0 and x.v_scale > 0
 
 
+# ------------------------------------------------------------- varlen prefill
+def _varlen_tiny():
+    kv, ql = [4, 1, 0, 6, 3], [2, 1, 0, 3, 3]  # includes a one-key sequence, an empty one, nq == nkv
+    x = workloads.varlen_inputs(kv, ql, seed=41, d=4)
+    return x, kv, ql
+
+
+def test_varlen_brute_force_tiny():
+    """Each sequence is brute-forced on its own slices with its queries at its last positions."""
+    x, kv, ql = _varlen_tiny()
+    o, lse = oracle.prefill_causal_varlen(x.q, x.k, x.v, x.cu_q, x.cu_kv, SCALE)
+    for i in range(len(kv)):
+        q0, q1, k0, k1 = x.cu_q[i], x.cu_q[i + 1], x.cu_kv[i], x.cu_kv[i + 1]
+        if q1 == q0:
+            continue
+        start = (k1 - k0) - (q1 - q0)
+        ref = _brute(x.q[q0:q1], x.k[k0:k1], x.v[k0:k1], lambda r, j: j <= start + r, SCALE, 6)
+        np.testing.assert_allclose(o[q0:q1], ref, atol=1e-12, rtol=0)
+    assert np.isfinite(lse).all()
+
+
+def test_varlen_sequences_are_independent():
+    """Changing one sequence's K/V leaves every other sequence bit-identical (and its lse too)."""
+    x, kv, ql = _varlen_tiny()
+    o, lse = oracle.prefill_causal_varlen(x.q, x.k, x.v, x.cu_q, x.cu_kv, SCALE)
+    k2, v2 = x.k.copy(), x.v.copy()
+    k0, k1 = x.cu_kv[3], x.cu_kv[4]
+    k2[k0:k1] += np.float16(0.5)
+    v2[k0:k1] *= np.float16(-1)
+    o2, lse2 = oracle.prefill_causal_varlen(x.q, k2, v2, x.cu_q, x.cu_kv, SCALE)
+    other = np.ones(x.q.shape[0], dtype=bool)
+    other[x.cu_q[3]:x.cu_q[4]] = False
+    assert np.array_equal(o[other], o2[other]) and np.array_equal(lse[other], lse2[other])
+    assert not np.array_equal(o[~other], o2[~other])
+
+
+def test_varlen_lse_is_log_partition():
+    """lse equals log sum_j exp(scale q.k_j) over the visible keys (closed form on one sequence)."""
+    x, kv, ql = _varlen_tiny()
+    _, lse = oracle.prefill_causal_varlen(x.q, x.k, x.v, x.cu_q, x.cu_kv, SCALE)
+    i = 3
+    q0, k0, nkv, nq = x.cu_q[i], x.cu_kv[i], kv[i], ql[i]
+    for r in range(nq):
+        for h in range(6):
+            vis = range(nkv - nq + r + 1)
+            z = math.fsum(math.exp(SCALE * math.fsum(float(x.q[q0 + r, h, t]) * float(x.k[k0 + j, 0, t])
+                                                     for t in range(4))) for j in vis)
+            assert abs(lse[q0 + r, h] - math.log(z)) < 1e-12
+
+
 # ------------------------------------------------------------- planted mistakes
 def _pin_suite():
     """Cheap pins run against a mutated oracle; returns the names that fail."""

@@ -65,6 +65,43 @@ def causal_inputs(nq: int, n_kv: int, seed: int, hq: int = HQ, hkv: int = HKV, d
     return q, k, v
 
 
+# ------------------------------------------------------------- varlen prefill
+@dataclass
+class VarlenInputs:
+    q: np.ndarray        # fp16 [total_q, hq, d]
+    k: np.ndarray        # fp16 [total_kv, hkv, d]
+    v: np.ndarray
+    cu_q: np.ndarray     # int32 [batch + 1]
+    cu_kv: np.ndarray    # int32 [batch + 1]
+    scale: float = SCALE
+
+
+def varlen_inputs(kv_lens, q_lens, seed: int, hq: int = HQ, hkv: int = HKV, d: int = D) -> VarlenInputs:
+    """A batch of sequences packed end to end: sequence i has kv_lens[i] keys and
+    q_lens[i] <= kv_lens[i] queries (its last positions).  Q, K, V are drawn in
+    that order from one seeded N(0,1) float32 stream and rounded to fp16."""
+    kv_lens = np.asarray(kv_lens, dtype=np.int64)
+    q_lens = np.asarray(q_lens, dtype=np.int64)
+    if (q_lens > kv_lens).any() or (q_lens < 0).any():
+        raise ValueError("each sequence needs 0 <= q_len <= kv_len")
+    rng = np.random.default_rng(seed)
+    cu_q = np.concatenate([[0], np.cumsum(q_lens)]).astype(np.int32)
+    cu_kv = np.concatenate([[0], np.cumsum(kv_lens)]).astype(np.int32)
+    q = _normal16(rng, (int(cu_q[-1]), hq, d))
+    k = _normal16(rng, (int(cu_kv[-1]), hkv, d))
+    v = _normal16(rng, (int(cu_kv[-1]), hkv, d))
+    return VarlenInputs(q=q, k=k, v=v, cu_q=cu_q, cu_kv=cu_kv)
+
+
+def varlen_batch_lengths(seed: int, batch: int = 8, kv_lo: int = 4096, kv_hi: int = 32768, q_frac: float = 0.25):
+    """Seeded request mix of a chunked-prefill batch: kv lengths uniform in
+    [kv_lo, kv_hi], each request prefilling the last q_frac of its tokens."""
+    rng = np.random.default_rng(seed)
+    kv = rng.integers(kv_lo, kv_hi + 1, size=batch)
+    q = np.maximum(1, (kv * q_frac).astype(np.int64))
+    return kv, q
+
+
 # ------------------------------------------------------- paged block-sparse prefill
 PAGE_SIZE = 16
 KV_BLOCK_TOKENS = 4
