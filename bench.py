@@ -19,8 +19,9 @@ Prints ONE JSON line.  Besides the driver's fields it carries
                 of query rows of the same workload, in the same unit;
   paths         the same measurement for the other entry points: the paged
                 block-sparse prefill (S = 64/512/2048), the paged dense causal
-                prefill (every block selected, pages of 16 and 784 tokens) and
-                the FP8 verifier tail (q = 2/4/8).
+                prefill (every block selected, pages of 16 and 784 tokens), the
+                FP8 verifier tail (q = 2/4/8) and the varlen causal prefill of
+                a chunked-prefill batch.
 
 `roofline.traffic` is the HBM traffic per launch of that kernel, read from the
 committed counter summary (profiles/hbm_traffic_per_launch.md) when the kernel
@@ -74,6 +75,10 @@ def paged_workload(select_tokens: int, tail: int = 1) -> str:
 
 def paged_dense_workload(page_size: int, tail: int = 1) -> str:
     return f"paged_dense_causal_q4096_page{page_size}_tail{tail}"
+
+
+def varlen_workload() -> str:
+    return "varlen_causal_prefill_batch8_kv4096to32768_q25pct"
 
 
 def verify_workload(nq: int) -> str:
@@ -134,8 +139,12 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
     workloads by the benchmark's fixed order: a step starts at prefill_causal_fwd,
     paged_prepass or verify_fwd, and each workload makes warmup + steps of them."""
     per = warmup + steps
-    first = {"prefill_causal_fwd": "prefill", "paged_prepass": "paged", "verify_fwd": "verify"}
-    labels = {"prefill": [prefill_workload(n_kv)],
+    family = {"prefill_causal_fwd": "prefill", "prefill_merge": "prefill",
+              "paged_prepass": "paged", "paged_fwd": "paged", "paged_merge": "paged",
+              "verify_fwd": "verify", "verify_merge": "verify",
+              "prefill_varlen_prepass": "varlen", "prefill_causal_varlen": "varlen", "prefill_merge_varlen": "varlen"}
+    first = {"prefill_causal_fwd", "paged_prepass", "verify_fwd", "prefill_varlen_prepass"}  # a step starts here
+    labels = {"prefill": [prefill_workload(n_kv)], "varlen": [varlen_workload()],
               "paged": [paged_workload(s) for s in PAGED_SELECTIONS] + [paged_dense_workload(p) for p in PAGED_DENSE_PAGES],
               "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
     true_kib = calib_mib * 1024.0
@@ -150,9 +159,9 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
         cur = None
         for _, name, v in rows:
             if name in first:
-                cur = first[name]
+                cur = family[name]
                 count[cur] += 1
-            if cur is None or not name.startswith(cur):
+            if cur is None or family.get(name) != cur:
                 continue
             wl = labels[cur][min((count[cur] - 1) // per, len(labels[cur]) - 1)]
             result.setdefault((name, wl), {}).setdefault(counter, []).append(v)
@@ -323,6 +332,40 @@ def bench_paged(select_tokens, steps, warmup, tail=1, seed=0, dense_page_size=No
     return line
 
 
+def bench_varlen(steps, warmup, seed=0):
+    """Varlen causal prefill of a chunked-prefill batch: 8 requests with kv lengths uniform in
+    [4096, 32768], each prefilling its last quarter (queries at the last positions)."""
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    kv, ql = workloads.varlen_batch_lengths(seed)
+    x = workloads.varlen_inputs(kv, ql, seed)
+    q, k, v = (torch.from_numpy(a).cuda() for a in (x.q, x.k, x.v))
+    cu_q, cu_kv = torch.from_numpy(x.cu_q).cuda(), torch.from_numpy(x.cu_kv).cuda()
+    o = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], 6), dtype=torch.float32, device="cuda")
+    ws = torch.empty(g.gqa_prefill_causal_varlen_workspace_size(len(kv), q.shape[0]), dtype=torch.uint8,
+                     device="cuda")
+
+    def step():
+        g.gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, x.scale, o=o, lse=lse, workspace=ws)
+
+    ms, kms = time_steps(step, steps, warmup)
+    pairs = int(sum(int(n) * (int(m) - int(n)) + int(n) * (int(n) + 1) // 2 for n, m in zip(ql, kv)))
+    flops = 4.0 * 256 * 6 * pairs
+    tf = flops / (kms * 1e-3) / 1e12
+    return {
+        "workload": varlen_workload(),
+        "kv_lens": [int(a) for a in kv], "q_lens": [int(a) for a in ql],
+        "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "prefill_causal_varlen", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 4),
+                     "traffic": recorded_traffic().get(("prefill_causal_varlen", varlen_workload()))},
+    }
+
+
 def bench_verify(nq, steps, warmup, copies=3, seed=0):
     import torch
 
@@ -439,6 +482,7 @@ def main(argv=None):
             "paged_sparse": [bench_paged(sel, args.steps, args.warmup) for sel in PAGED_SELECTIONS],
             "paged_dense": [bench_paged(None, args.steps, args.warmup, dense_page_size=ps) for ps in PAGED_DENSE_PAGES],
             "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in VERIFY_QUERIES],
+            "varlen": [bench_varlen(args.steps, args.warmup)],
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(cfg, r["host"], args.cpu_seconds)

@@ -31,6 +31,10 @@ SIGNATURES = {
     "gqa_prefill_paged_sparse_dropped": (_i32, [_vp, _i32p, _vp]),
     "gqa_verify_fp8kv_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _szp]),
     "gqa_verify_fp8kv": (_i32, [_vp, _vp, _vp, _f32, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gqa_prefill_causal_varlen_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
+    "gqa_prefill_causal_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
+                                         ctypes.c_float, _vp, ctypes.c_size_t, _vp]),
+    "gqa_prefill_causal_varlen_skipped": (_i32, [_vp, _i32p, _vp]),
     "gqa_profile_start": (_i32, []),
     "gqa_profile_stop": (_i32, [ctypes.POINTER(ctypes.c_double), _i32p]),
     "gqa_profile_clock_mhz": (_i32, [ctypes.POINTER(ctypes.c_double)]),
@@ -135,6 +139,50 @@ def gqa_prefill_causal(q, k, v, q_pos0: int, scale: float, o=None, workspace=Non
                                   _stream(stream))
     _check(st, "gqa_prefill_causal")
     return o
+
+
+# --------------------------------------------------------------- varlen prefill
+def gqa_prefill_causal_varlen_workspace_size(batch: int, total_q: int, hq: int = 6, hkv: int = 1, d: int = 256) -> int:
+    out = ctypes.c_size_t(0)
+    _check(lib().gqa_prefill_causal_varlen_workspace_size(batch, total_q, hq, hkv, d, ctypes.byref(out)),
+           "gqa_prefill_causal_varlen_workspace_size")
+    return out.value
+
+
+def gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, scale: float, o=None, lse=None, want_lse: bool = True,
+                              workspace=None, stream=None):
+    """Causal prefill of a packed batch; q [total_q, Hq, D], k/v [total_kv, Hkv, D] fp16, cu_q/cu_kv int32
+    [batch + 1] on device -> (o [total_q, Hq, D], lse [total_q, Hq] fp32 or None)."""
+    import torch
+
+    total_q, hq, d = q.shape
+    total_kv, hkv, _ = k.shape
+    if tuple(v.shape) != tuple(k.shape):
+        raise ValueError("k and v must have the same shape")
+    batch = cu_q.numel() - 1
+    if cu_kv.numel() != batch + 1:
+        raise ValueError("cu_q and cu_kv must have the same length")
+    if o is None:
+        o = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((total_q, hq), dtype=torch.float32, device=q.device)
+    nbytes = gqa_prefill_causal_varlen_workspace_size(batch, total_q, hq, hkv, d)
+    ws, ws_bytes = _workspace(nbytes, q.device, workspace)
+    st = lib().gqa_prefill_causal_varlen(
+        _dev(q, torch.float16, "q"), _dev(k, torch.float16, "k"), _dev(v, torch.float16, "v"),
+        _dev(o, torch.float16, "o"), None if lse is None else _dev(lse, torch.float32, "lse"),
+        _dev(cu_q, torch.int32, "cu_q"), _dev(cu_kv, torch.int32, "cu_kv"), batch, total_q, total_kv, hq, hkv, d,
+        scale, ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream(stream))
+    _check(st, "gqa_prefill_causal_varlen")
+    return o, lse, ws
+
+
+def gqa_prefill_causal_varlen_skipped(workspace, stream=None) -> int:
+    """Sequences the last varlen call on `workspace` skipped as invalid (synchronises the stream)."""
+    n = ctypes.c_int32(0)
+    _check(lib().gqa_prefill_causal_varlen_skipped(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(n),
+                                                   _stream(stream)), "gqa_prefill_causal_varlen_skipped")
+    return n.value
 
 
 # --------------------------------------------------------------- kernel timing

@@ -189,6 +189,58 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
                                                (hipStream_t)stream));
 }
 
+// ------------------------------------------------------------ varlen prefill
+namespace {
+constexpr int32_t kMaxBatch = 1 << 20;
+
+gqa_status varlen_sizes(int32_t batch, int32_t total_q, int32_t total_kv, int32_t hq, int32_t hkv, int32_t d) {
+  if (batch <= 0 || total_q < 0 || total_kv < 0) return GQA_ERR_INVALID;
+  gqa_status st = check_shape(hq, hkv, d);
+  if (st != GQA_OK) return st;
+  if (batch > kMaxBatch || !rows_fit((int64_t)total_q * hq, 2 * d) || !rows_fit(total_kv, 2 * d))
+    return GQA_ERR_UNSUPPORTED;
+  return GQA_OK;
+}
+}  // namespace
+
+gqa_status gqa_prefill_causal_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t hq, int32_t hkv,
+                                                    int32_t d, size_t* bytes) {
+  if (!bytes) return GQA_ERR_INVALID;
+  gqa_status st = varlen_sizes(batch, total_q, 0, hq, hkv, d);
+  if (st != GQA_OK) return st;
+  const size_t w = gqa::prefill_varlen_workspace_bytes(gqa::prefill_varlen_schedule(batch, total_q));
+  if ((int64_t)w > kMaxBufferBytes) return GQA_ERR_UNSUPPORTED;
+  *bytes = w;
+  return GQA_OK;
+}
+
+gqa_status gqa_prefill_causal_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, int32_t total_q,
+                                     int32_t total_kv, int32_t hq, int32_t hkv, int32_t d, float scale,
+                                     void* workspace, size_t workspace_bytes, void* stream) {
+  if (!q || !k || !v || !o || !cu_q || !cu_kv) return GQA_ERR_INVALID;
+  if (!good_scale(scale)) return GQA_ERR_INVALID;
+  gqa_status st = varlen_sizes(batch, total_q, total_kv, hq, hkv, d);
+  if (st != GQA_OK) return st;
+  size_t need = 0;
+  st = gqa_prefill_causal_varlen_workspace_size(batch, total_q, hq, hkv, d, &need);
+  if (st != GQA_OK) return st;
+  if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;
+  return hip_status(gqa::launch_prefill_causal_varlen(q, k, v, o, lse, cu_q, cu_kv, batch, total_q, total_kv, scale,
+                                                      workspace, (hipStream_t)stream));
+}
+
+gqa_status gqa_prefill_causal_varlen_skipped(const void* workspace, int32_t* count, void* stream) {
+  if (!workspace || !count) return GQA_ERR_INVALID;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t hdr[4] = {0, 0, 0, 0};
+  hipError_t e = hipMemcpyAsync(hdr, workspace, sizeof(hdr), hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_status(e);
+  *count = hdr[1];
+  return GQA_OK;
+}
+
 // ------------------------------------------------------- paged block-sparse
 namespace {
 gqa_status paged_sizes(int32_t nq, int32_t n_block_ids, int32_t qblock_rows, int32_t kv_block_tokens, int32_t hq,

@@ -49,9 +49,19 @@ struct PrefillParams {
   int grid;
   int split;  // key-split pieces per q-block (0: stream-K split)
   unsigned long long* clk;  // profiling: {shader cycles, wall ticks} accumulator, or null
+  float* lse;               // per packed row log-sum-exp (natural log), or null
+  const int* vdesc;         // varlen: block descriptors (see prefill_varlen_prepass), else null
   uint32_t part_bytes;
   float c;  // scale * log2(e): scores are kept in log2 units
 };
+
+constexpr float kLn2 = 0.69314718055994531f;
+
+// log sum_j exp(scale q.k_j) of a row from its online-softmax state: m is the
+// reference maximum and l the sum of 2^(t_j - m), both in log2 units.
+__device__ __forceinline__ float row_lse(float m, float l) {
+  return (l > 0.f) ? (m + __builtin_log2f(l)) * kLn2 : -INFINITY;
+}
 
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
@@ -190,6 +200,13 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
     const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
 #pragma unroll
     for (int c = 0; c < C; ++c) store_rows_f16(ro, row_base + 32 * c + col, half, acc[c], lt[c], 1.0f);
+    if (p.lse != nullptr && half == 0) {
+      const rsrc_t rl = make_rsrc(p.lse, (uint32_t)p.nrows * 4);
+#pragma unroll
+      for (int c = 0; c < C; ++c)
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(row_lse(m[c], lt[c])), rl,
+                                              (uint32_t)(row_base + 32 * c + col) * 4, 0, 0);
+    }
   } else {
     const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
     const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
@@ -263,7 +280,49 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p)
 }
 
 // Exact merge of the partials of q-blocks that were split across workgroups:
-// M = max_k m_k, O = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k.
+// M = max_k m_k, O = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k, and
+// lse = (M + log2 sum_k 2^(m_k - M) l_k) ln 2.  Thread (row rl of the slots,
+// 64 columns from 64*dq) combines slots slot_lo .. slot_hi into output row
+// `orow` of p.o (and p.lse).
+__device__ __forceinline__ void merge_row(const PrefillParams& p, int slot_lo, int slot_hi, int rl, int dq, int orow) {
+  const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+  float M = -INFINITY;
+  for (int w = slot_lo; w <= slot_hi; ++w) {
+    const uint32_t sb = (uint32_t)w * (uint32_t)(kPartialFloats * 4);
+    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0)));
+  }
+  f4 o[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+  for (int w = slot_lo; w <= slot_hi; ++w) {
+    const uint32_t sb = (uint32_t)w * (uint32_t)(kPartialFloats * 4);
+    const float mw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
+    const float lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
+    const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
+    L += aw * lw;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((16 * dq + j) * kRowsPerBlock + rl) * 16), 0, 0);
+      o[j] += aw * __builtin_bit_cast(f4, x);
+    }
+  }
+  const float inv = L > 0.f ? 1.0f / L : 0.f;
+  const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+  const uint32_t obase = (uint32_t)orow * kRowBytes + 128 * dq;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) {
+    const h2 a0 = cvt2(o[j][0] * inv, o[j][1] * inv), a1 = cvt2(o[j][2] * inv, o[j][3] * inv);
+    const h2 b0 = cvt2(o[j + 1][0] * inv, o[j + 1][1] * inv), b1 = cvt2(o[j + 1][2] * inv, o[j + 1][3] * inv);
+    const h8 x = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    store_16B(ro, obase + j * 8, __builtin_bit_cast(u4, x));
+  }
+  if (p.lse != nullptr && dq == 0) {
+    const rsrc_t rl_ = make_rsrc(p.lse, (uint32_t)p.nrows * 4);
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(row_lse(M, L)), rl_, (uint32_t)orow * 4, 0, 0);
+  }
+}
+
 // Workgroup (b, quarter): 64 rows of q-block b; thread (row, 64 columns).
 __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   constexpr int kParts = kRowsPerBlock / 64;
@@ -285,39 +344,141 @@ __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   if (w0 == w1) return;  // done whole by one workgroup, already written
   const int tid = threadIdx.x;
   const int rl = quarter * 64 + (tid & 63);
-  const int dq = tid >> 6;  // columns 64*dq .. 64*dq+63
-  const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-  float M = -INFINITY;
-  for (int w = w0; w <= w1; ++w) {
-    const uint32_t sb = (uint32_t)(w + slot0) * (uint32_t)(kPartialFloats * 4);
-    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0)));
-  }
-  f4 o[16];
-#pragma unroll
-  for (int j = 0; j < 16; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int w = w0; w <= w1; ++w) {
-    const uint32_t sb = (uint32_t)(w + slot0) * (uint32_t)(kPartialFloats * 4);
-    const float mw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
-    const float lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
-    const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-    L += aw * lw;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((16 * dq + j) * kRowsPerBlock + rl) * 16), 0, 0);
-      o[j] += aw * __builtin_bit_cast(f4, x);
+  merge_row(p, w0 + slot0, w1 + slot0, rl, tid >> 6, b * kRowsPerBlock + rl);
+}
+
+// ------------------------------------------------------------------ varlen
+// A batch of independent sequences packed end to end: sequence i owns query
+// tokens cu_q[i] .. cu_q[i+1]-1 and keys cu_kv[i] .. cu_kv[i+1]-1, its queries
+// at its last positions.  Its 6 nq_i packed rows are cut into q-blocks of 256
+// rows; a one-workgroup prepass writes one descriptor per q-block (the first
+// query token and key of its sequence, nq_i, nkv_i, the q-block's index in the
+// sequence); descriptors past the last q-block get nq = 0.  A sequence whose
+// offsets are out of order or out of range, or that has more queries than
+// keys, gets no q-blocks and is counted in the header; its rows are not
+// written.  Every q-block is split into `split` key ranges as in the dense
+// kernel, and each (q-block, range) workgroup runs the dense 32-row-per-wave
+// step on its sequence's slices.
+constexpr int kVDescInts = 8;
+
+struct VarlenPrepass {
+  const int* cu_q;
+  const int* cu_kv;
+  int* desc;
+  int* hdr;  // [0] q-blocks used, [1] sequences skipped as invalid
+  int batch, total_q, total_kv, cap;
+};
+
+__global__ __launch_bounds__(256) void prefill_varlen_prepass(VarlenPrepass v) {
+  __shared__ int scan[256];
+  const int tid = threadIdx.x;
+  const rsrc_t rq = make_rsrc(v.cu_q, (uint32_t)(v.batch + 1) * 4);
+  const rsrc_t rk = make_rsrc(v.cu_kv, (uint32_t)(v.batch + 1) * 4);
+  const rsrc_t rd = make_rsrc(v.desc, (uint32_t)v.cap * kVDescInts * 4);
+  int base = 0, bad = 0;
+  for (int s0 = 0; s0 < v.batch; s0 += 256) {
+    const int i = s0 + tid;
+    int cnt = 0, q0 = 0, nq = 0, k0 = 0, nkv = 0;
+    if (i < v.batch) {
+      q0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, i * 4, 0, 0);
+      const int q1 = (int)__builtin_amdgcn_raw_buffer_load_b32(rq, (i + 1) * 4, 0, 0);
+      k0 = (int)__builtin_amdgcn_raw_buffer_load_b32(rk, i * 4, 0, 0);
+      const int k1 = (int)__builtin_amdgcn_raw_buffer_load_b32(rk, (i + 1) * 4, 0, 0);
+      nq = q1 - q0;
+      nkv = k1 - k0;
+      const bool ok = q0 >= 0 && q0 <= q1 && q1 <= v.total_q && k0 >= 0 && k0 <= k1 && k1 <= v.total_kv && nq <= nkv;
+      if (ok)
+        cnt = (6 * nq + kRowsPerBlock - 1) / kRowsPerBlock;
+      else
+        bad += 1;
     }
+    // inclusive scan of the q-block counts over the 256 threads
+    scan[tid] = cnt;
+    __syncthreads();
+    for (int d = 1; d < 256; d <<= 1) {
+      const int x = tid >= d ? scan[tid - d] : 0;
+      __syncthreads();
+      scan[tid] += x;
+      __syncthreads();
+    }
+    const int first = base + scan[tid] - cnt;
+    for (int j = 0; j < cnt; ++j) {
+      const int e = first + j;
+      if (e >= v.cap) break;
+      const uint32_t off = (uint32_t)e * kVDescInts * 4;
+      __builtin_amdgcn_raw_buffer_store_b32((unsigned)q0, rd, off, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((unsigned)nq, rd, off + 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((unsigned)k0, rd, off + 8, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((unsigned)nkv, rd, off + 12, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32((unsigned)j, rd, off + 16, 0, 0);
+    }
+    base += scan[255];
+    __syncthreads();
   }
-  const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-  const uint32_t obase = (uint32_t)(b * kRowsPerBlock + rl) * kRowBytes + 128 * dq;
+  const int used = min(base, v.cap);
+  for (int e = used + tid; e < v.cap; e += 256)
+    __builtin_amdgcn_raw_buffer_store_b32(0u, rd, (uint32_t)e * kVDescInts * 4 + 4, 0, 0);  // nq = 0: unused
+  scan[tid] = bad;
+  __syncthreads();
+  if (tid == 0) {
+    int nbad = 0;
+    for (int t = 0; t < 256; ++t) nbad += scan[t];
+    v.hdr[0] = used;
+    v.hdr[1] = nbad;
+  }
+}
+
+// The dense parameters narrowed to the sequence of varlen q-block qb (false
+// when the descriptor is unused).
+__device__ __forceinline__ bool varlen_block(const PrefillParams& p, int qb, PrefillParams& s, int& jblk) {
+  const int* d = p.vdesc + qb * kVDescInts;
+  const int q0 = d[0], nq = d[1], k0 = d[2], nkv = d[3];
+  jblk = d[4];
+  if (nq <= 0) return false;
+  s = p;
+  s.q = p.q + (size_t)q0 * kGroup * kHeadDim;
+  s.o = p.o + (size_t)q0 * kGroup * kHeadDim;
+  s.lse = p.lse != nullptr ? p.lse + (size_t)q0 * kGroup : nullptr;
+  s.k = p.k + (size_t)k0 * kHeadDim;
+  s.v = p.v + (size_t)k0 * kHeadDim;
+  s.nrows = nq * kGroup;
+  s.q_pos0 = nkv - nq;
+  s.kv_live = nkv;
+  return true;
+}
+
+__global__ __launch_bounds__(512, 1) void prefill_causal_varlen(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char smem[4 * kTileBytes];
+  const int qb = blockIdx.x / p.split, j = blockIdx.x % p.split;
+  PrefillParams s;
+  int jblk;
+  if (!varlen_block(p, qb, s, jblk)) return;
+  const int nt = prefill_block_tiles(jblk, s.nrows, s.q_pos0);
+  const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
+  if (lo >= hi) {  // a short q-block has fewer tiles than pieces: leave the empty state
+    const int tid = threadIdx.x, lane = tid & 63;
+    f16x z[8];
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) {
-    const h2 a0 = cvt2(o[j][0] * inv, o[j][1] * inv), a1 = cvt2(o[j][2] * inv, o[j][3] * inv);
-    const h2 b0 = cvt2(o[j + 1][0] * inv, o[j + 1][1] * inv), b1 = cvt2(o[j + 1][2] * inv, o[j + 1][3] * inv);
-    const h8 x = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-    store_16B(ro, obase + j * 8, __builtin_bit_cast(u4, x));
+    for (int dt = 0; dt < 8; ++dt) z[dt] = f16x{};
+    store_partial(make_rsrc(p.part, p.part_bytes), (uint32_t)blockIdx.x * (uint32_t)(kPartialFloats * 4),
+                  kRowsPerBlock, (tid >> 6) * 32 + (lane & 31), lane >> 5, z, -INFINITY, 0.f);
+    return;
   }
+  prefill_piece<1, 8>(s, smem, jblk, lo, hi, p.split == 1, blockIdx.x);
+}
+
+__global__ __launch_bounds__(256) void prefill_merge_varlen(PrefillParams p) {
+  constexpr int kParts = kRowsPerBlock / 64;
+  const int qb = blockIdx.x / kParts;
+  const int quarter = blockIdx.x % kParts;
+  PrefillParams s;
+  int jblk;
+  if (!varlen_block(p, qb, s, jblk)) return;
+  const int tid = threadIdx.x;
+  const int rl = quarter * 64 + (tid & 63);
+  const int orow = jblk * kRowsPerBlock + rl;
+  if (orow >= s.nrows) return;
+  merge_row(s, qb * p.split, qb * p.split + p.split - 1, rl, tid >> 6, orow);
 }
 
 }  // namespace
@@ -342,6 +503,8 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
   p.c = scale * kLog2e;
   p.clk = prof_clock();
+  p.lse = nullptr;
+  p.vdesc = nullptr;
   prof_before(stream);
   hipLaunchKernelGGL((prefill_causal_fwd<kPrefillC, kPrefillW>), dim3(s.grid), dim3(64 * kPrefillW), 0, stream, p);
   hipError_t e = hipGetLastError();
@@ -352,6 +515,50 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
     e = hipGetLastError();
   }
   return e;
+}
+
+hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                        const int32_t* cu_q, const int32_t* cu_kv, int batch, int total_q,
+                                        int total_kv, float scale, void* workspace, hipStream_t stream) {
+  const VarlenSched vs = prefill_varlen_schedule(batch, total_q);
+  char* ws = (char*)workspace;
+  VarlenPrepass pre;
+  pre.cu_q = cu_q;
+  pre.cu_kv = cu_kv;
+  pre.hdr = (int*)ws;
+  pre.desc = (int*)(ws + kVarlenHeaderBytes);
+  pre.batch = batch;
+  pre.total_q = total_q;
+  pre.total_kv = total_kv;
+  pre.cap = vs.cap;
+  hipLaunchKernelGGL(prefill_varlen_prepass, dim3(1), dim3(256), 0, stream, pre);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  PrefillParams p;
+  p.q = (const _Float16*)q;
+  p.k = (const _Float16*)k;
+  p.v = (const _Float16*)v;
+  p.o = (_Float16*)o;
+  p.part = (float*)(ws + varlen_part_offset(vs));
+  p.part_bytes = (uint32_t)((size_t)vs.cap * vs.split * kPartialFloats * 4);
+  p.total = 0;
+  p.nrows = 0;
+  p.kv_live = 0;
+  p.q_pos0 = 0;
+  p.nqb = vs.cap;
+  p.grid = vs.cap * vs.split;
+  p.split = vs.split;
+  p.c = scale * kLog2e;
+  p.clk = nullptr;
+  p.lse = lse;
+  p.vdesc = pre.desc;
+  prof_before(stream);
+  hipLaunchKernelGGL(prefill_causal_varlen, dim3(p.grid), dim3(512), 0, stream, p);
+  e = hipGetLastError();
+  prof_after(stream);
+  if (e != hipSuccess || vs.split == 1) return e;
+  hipLaunchKernelGGL(prefill_merge_varlen, dim3(vs.cap * (kRowsPerBlock / 64)), dim3(256), 0, stream, p);
+  return hipGetLastError();
 }
 
 }  // namespace gqa

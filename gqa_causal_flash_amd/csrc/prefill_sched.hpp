@@ -121,4 +121,38 @@ inline size_t prefill_workspace_bytes(const PrefillSched& s) {
   return (size_t)(s.grid + s.nqb) * kPartialFloats * sizeof(float);
 }
 
+// Varlen prefill (a batch of sequences packed end to end): the q-blocks of
+// all sequences number at most cap = ceil(6 total_q / 256) + batch (each
+// sequence adds at most one partial q-block), which sizes the grid before the
+// sequence lengths, held in device memory, are known.  Every q-block is cut
+// into `split` key ranges: the smallest power of two (<= 8) giving at least
+// four workgroups per compute unit, since q-blocks of sequences of different
+// lengths carry different amounts of work and finer pieces even them out.
+// Workspace: header (16 B: q-blocks used, sequences skipped), cap descriptors
+// of 8 int32, then cap * split partial slots when split > 1.
+constexpr size_t kVarlenHeaderBytes = 16;
+
+struct VarlenSched {
+  int cap;
+  int split;
+};
+
+inline VarlenSched prefill_varlen_schedule(int batch, int total_q) {
+  VarlenSched s;
+  s.cap = (int)((6LL * total_q + kRowsPerBlock - 1) / kRowsPerBlock) + batch;
+  int sp = 1;
+  while (sp < 8 && (long long)s.cap * sp < 4LL * kTargetGrid) sp *= 2;
+  s.split = sp;
+  return s;
+}
+
+inline size_t varlen_part_offset(const VarlenSched& s) {
+  return (kVarlenHeaderBytes + (size_t)s.cap * 8 * sizeof(int) + 255) / 256 * 256;
+}
+
+inline size_t prefill_varlen_workspace_bytes(const VarlenSched& s) {
+  const size_t parts = s.split > 1 ? (size_t)s.cap * s.split * kPartialFloats * sizeof(float) : 0;
+  return varlen_part_offset(s) + parts;
+}
+
 }  // namespace gqa

@@ -82,6 +82,43 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Varlen causal prefill: a batch of independent sequences packed end to end.
+ *
+ * The dense causal prefill above, applied to each sequence of a batch the
+ * way a serving engine packs requests (the long-prefill page measures the
+ * operator under serving, Test Result), with the per-row log-sum-exp
+ * returned so that a caller can merge the result with other attention
+ * pieces (the exact online-softmax merge of the same page, Purpose).
+ *
+ *   q, o   [total_q][hq][d] fp16;  k, v [total_kv][hkv][d] fp16
+ *   cu_q, cu_kv [batch + 1] int32 in device memory: sequence i owns query
+ *          tokens cu_q[i] .. cu_q[i+1]-1 and keys cu_kv[i] .. cu_kv[i+1]-1;
+ *          its nq_i queries sit at its last nq_i positions (query j of the
+ *          sequence sees its keys 0 .. nkv_i - nq_i + j).  Requires
+ *          0 <= cu_q[i] <= cu_q[i+1] <= total_q, the same for cu_kv with
+ *          total_kv, and nq_i <= nkv_i; a sequence that breaks this is
+ *          skipped (its rows of o and lse are not written) and counted,
+ *          see gqa_prefill_causal_varlen_skipped().  Sequences may be empty.
+ *   lse    [total_q][hq] fp32 or NULL: natural-log log-sum-exp of each row's
+ *          scaled scores, log sum_j exp(scale * q . k_j).
+ *   The workspace holds the per-block schedule the device builds from the
+ *   offsets and the split-KV partials; its size depends on batch and total_q
+ *   only.  Same shape family and errors as gqa_prefill_causal; batch must be
+ *   in [1, 2^20].
+ * ------------------------------------------------------------------------ */
+gqa_status gqa_prefill_causal_varlen_workspace_size(int32_t batch, int32_t total_q, int32_t hq, int32_t hkv,
+                                                    int32_t d, size_t* bytes);
+
+gqa_status gqa_prefill_causal_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
+                                     const int32_t* cu_q, const int32_t* cu_kv, int32_t batch, int32_t total_q,
+                                     int32_t total_kv, int32_t hq, int32_t hkv, int32_t d, float scale,
+                                     void* workspace, size_t workspace_bytes, void* stream);
+
+/* Number of sequences the last varlen call on `workspace` skipped as
+ * invalid (synchronises `stream`). */
+gqa_status gqa_prefill_causal_varlen_skipped(const void* workspace, int32_t* count, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Paged block-sparse causal prefill.
  *
  * Defined by the block-sparse page ("[Kernel][SM70] Repair #378 on latest

@@ -154,3 +154,36 @@ def test_profile_clock_before_any_session_is_zero():
     assert g.lib().gqa_profile_clock_mhz(ctypes.byref(mhz)) == g.GQA_OK
     assert mhz.value == 0.0
     assert g.lib().gqa_profile_clock_mhz(None) == g.GQA_ERR_INVALID
+
+
+def _varlen(**kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, o=FAKE, lse=None, cu_q=FAKE, cu_kv=FAKE, batch=3, total_q=100, total_kv=300,
+             hq=6, hkv=1, d=256, scale=0.0625, ws=None, ws_bytes=0)
+    a.update(kw)
+    return g.lib().gqa_prefill_causal_varlen(a["q"], a["k"], a["v"], a["o"], a["lse"], a["cu_q"], a["cu_kv"],
+                                             a["batch"], a["total_q"], a["total_kv"], a["hq"], a["hkv"], a["d"],
+                                             a["scale"], a["ws"], a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), g.GQA_ERR_INVALID),
+    (dict(cu_q=None), g.GQA_ERR_INVALID),
+    (dict(cu_kv=None), g.GQA_ERR_INVALID),
+    (dict(batch=0), g.GQA_ERR_INVALID),
+    (dict(total_q=-1), g.GQA_ERR_INVALID),
+    (dict(scale=float("nan")), g.GQA_ERR_INVALID),
+    (dict(hq=8), g.GQA_ERR_UNSUPPORTED),
+    (dict(batch=(1 << 20) + 1), g.GQA_ERR_UNSUPPORTED),
+    (dict(), g.GQA_ERR_WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=16), g.GQA_ERR_WORKSPACE),
+])
+def test_varlen_rejects_before_launch(kw, status):
+    assert _varlen(**kw) == status
+
+
+def test_varlen_workspace_query():
+    n = ctypes.c_size_t()
+    assert g.lib().gqa_prefill_causal_varlen_workspace_size(8, 40000, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
+    assert n.value > 0
+    assert g.lib().gqa_prefill_causal_varlen_workspace_size(0, 10, 6, 1, 256, ctypes.byref(n)) == g.GQA_ERR_INVALID
+    assert g.lib().gqa_prefill_causal_varlen_skipped(None, ctypes.byref(ctypes.c_int32()), None) == g.GQA_ERR_INVALID

@@ -109,3 +109,24 @@ def test_graph_verify_fp8kv(nq):
         return g.gqa_verify_fp8kv(q, kb, vb, x.k_scale, x.v_scale, x.scale).clone()
 
     _replay_matches(graph, out, eager, refresh)
+
+
+def test_graph_prefill_causal_varlen():
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    x = workloads.varlen_inputs([3000, 1, 5000], [700, 1, 2000], seed=24)
+    q, k, v = to_dev(x.q), to_dev(x.k), to_dev(x.v)
+    cu_q, cu_kv = to_dev(x.cu_q), to_dev(x.cu_kv)
+    ws = torch.empty(g.gqa_prefill_causal_varlen_workspace_size(3, q.shape[0]), dtype=torch.uint8, device="cuda")
+    out = torch.empty_like(q)
+    lse = torch.empty((q.shape[0], 6), dtype=torch.float32, device="cuda")
+    eager = g.gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, x.scale)[0].clone()
+    graph = _capture(lambda: g.gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, x.scale, o=out, lse=lse, workspace=ws))
+
+    def refresh():
+        q.mul_(-0.5)
+        return g.gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, x.scale)[0].clone()
+
+    _replay_matches(graph, out, eager, refresh)
