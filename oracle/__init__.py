@@ -25,6 +25,10 @@ heads, head dim D, softmax scale, causal positions):
   cache stored as OCP E4M3 bytes with one fp32 scale per tensor ("[Perf] Ship
   the qualified SM70 long-context layout...", What / Changes: grouped E4M3 FP32
   long-context operator, verifier tail query_rows 2..8).
+* ``prefill_causal_e4m3`` -- the dense causal prefill with Q, K and V all given
+  as E4M3 codes and one fp32 scale per tensor: the quantised-Q definition of an
+  E4M3-cache long prefill whose Q K^T products run on FP8 matrix cores (same
+  page, What: grouped E4M3 FP32 long-context operator).
 * ``e4m3_decode`` -- the OCP 8-bit E4M3 ("E4M3FN") format definition.
 
 Every function returns unrounded float64 outputs together with the per-row
@@ -37,6 +41,7 @@ from .attention import (
     causal_visible,
     kv_head_of,
     prefill_causal,
+    prefill_causal_e4m3,
     prefill_causal_varlen,
     prefill_paged_sparse,
     verify_fp8kv,
@@ -49,6 +54,7 @@ __all__ = [
     "causal_visible",
     "kv_head_of",
     "prefill_causal",
+    "prefill_causal_e4m3",
     "prefill_causal_varlen",
     "prefill_paged_sparse",
     "verify_fp8kv",

@@ -219,6 +219,25 @@ def verify_fp8kv(q, k_bytes, v_bytes, k_scale: float, v_scale: float, scale: flo
     return prefill_causal(q, kd, vd, L - nq, scale, rows=rows)
 
 
+def prefill_causal_e4m3(q_bytes, q_scale: float, k_bytes, k_scale: float, v_bytes, v_scale: float, q_pos0: int,
+                        scale: float, rows=None):
+    """Dense causal GQA prefill over E4M3 inputs.
+
+    The long-context page's E4M3 operator ("[Perf] Ship the qualified SM70
+    long-context layout...", What: grouped E4M3 FP32 long-context operator)
+    keeps K and V as OCP E4M3 codes with one fp32 scale per tensor.  In the
+    variant whose Q K^T products run on FP8 matrix cores, Q is quantised the
+    same way, so the operation is defined on the quantised queries: every
+    operand is decode(byte) * its tensor's scale, and the attention is the
+    dense causal prefill (``prefill_causal``) of those values, with query row
+    r at position q_pos0 + r.  Returns (o [nq, Hq, D], lse [nq, Hq]).
+    """
+    qd = e4m3_decode(q_bytes) * np.float64(np.float32(q_scale))
+    kd = e4m3_decode(k_bytes) * np.float64(np.float32(k_scale))
+    vd = e4m3_decode(v_bytes) * np.float64(np.float32(v_scale))
+    return prefill_causal(qd, kd, vd, q_pos0, scale, rows=rows)
+
+
 def visible_pairs_causal(nq: int, n_kv: int, q_pos0: int) -> int:
     """Number of visible (query row, key) pairs of one head in causal prefill."""
     p0, p1 = q_pos0, q_pos0 + nq - 1

@@ -369,6 +369,56 @@ def test_verify_generator_scale_is_amax_over_448():
     assert x.k_scale > 0 and x.v_scale > 0
 
 
+# -------------------------------------------------------- E4M3 causal prefill
+def _torch_dec(codes, scale):
+    return torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy() * np.float64(np.float32(scale))
+
+
+def test_prefill_e4m3_equals_sdpa_on_torch_decoded_values():
+    """The E4M3 prefill is causal attention of decode(byte) * scale for Q, K and V
+    (torch's float8 decoding and torch SDPA as the library routines)."""
+    x = workloads.e4m3_prefill_inputs(24, 70, seed=51, d=32)
+    o, lse = oracle.prefill_causal_e4m3(x.q_bytes, x.q_scale, x.k_bytes, x.k_scale, x.v_bytes, x.v_scale,
+                                        x.q_pos0, x.scale)
+    ref = _torch_sdpa(_torch_dec(x.q_bytes, x.q_scale), _torch_dec(x.k_bytes, x.k_scale),
+                      _torch_dec(x.v_bytes, x.v_scale), x.q_pos0, x.scale)
+    np.testing.assert_allclose(o, ref, atol=1e-13, rtol=0)
+
+
+def test_prefill_e4m3_brute_force_tiny():
+    """Pure-Python attention over the spec decoding of the codes."""
+    x = workloads.e4m3_prefill_inputs(4, 7, seed=52, d=4)
+    o, _ = oracle.prefill_causal_e4m3(x.q_bytes, x.q_scale, x.k_bytes, x.k_scale, x.v_bytes, x.v_scale,
+                                      x.q_pos0, x.scale)
+    t = oracle.e4m3_table()
+    dec = lambda b, sc: np.vectorize(lambda c: float(t[c]) * float(np.float32(sc)))(b)
+    ref = _brute(dec(x.q_bytes, x.q_scale), dec(x.k_bytes, x.k_scale), dec(x.v_bytes, x.v_scale),
+                 lambda r, j: j <= x.q_pos0 + r, x.scale, 6)
+    np.testing.assert_allclose(o, ref, atol=1e-12, rtol=0)
+
+
+def test_prefill_e4m3_scales_enter_where_the_definition_puts_them():
+    """Doubling the Q scale while halving the softmax scale changes nothing; doubling
+    the V scale doubles O; doubling the K scale is the same as doubling the softmax scale."""
+    x = workloads.e4m3_prefill_inputs(6, 20, seed=53, d=8)
+    args = (x.q_bytes, x.q_scale, x.k_bytes, x.k_scale, x.v_bytes, x.v_scale, x.q_pos0)
+    o, lse = oracle.prefill_causal_e4m3(*args, x.scale)
+    o2, lse2 = oracle.prefill_causal_e4m3(x.q_bytes, 2 * x.q_scale, *args[2:], x.scale / 2)
+    assert np.array_equal(o, o2) and np.array_equal(lse, lse2)
+    o3, _ = oracle.prefill_causal_e4m3(*args[:5], 2 * x.v_scale, x.q_pos0, x.scale)
+    assert np.array_equal(o3, 2 * o)
+    o4, _ = oracle.prefill_causal_e4m3(x.q_bytes, x.q_scale, x.k_bytes, 2 * x.k_scale, *args[4:], x.scale)
+    o5, _ = oracle.prefill_causal_e4m3(*args, 2 * x.scale)
+    assert np.array_equal(o4, o5)
+
+
+def test_e4m3_prefill_generator_scales_are_amax_over_448():
+    x = workloads.e4m3_prefill_inputs(5, 30, seed=54, d=16)
+    for b in (x.q_bytes, x.k_bytes, x.v_bytes):
+        assert np.abs(oracle.e4m3_decode(b)).max() == 448.0
+    assert x.q_pos0 == 25 and min(x.q_scale, x.k_scale, x.v_scale) > 0
+
+
 # ------------------------------------------------------------- varlen prefill
 def _varlen_tiny():
     kv, ql = [4, 1, 0, 6, 3], [2, 1, 0, 3, 3]  # includes a one-key sequence, an empty one, nq == nkv

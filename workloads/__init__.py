@@ -18,6 +18,9 @@ even).  Shapes follow the workloads of the pages:
   qualified SM70 long-context layout...", Changes and Measurement).  The E4M3
   codes are produced with torch's float8_e4m3fn cast (round to nearest even)
   of value/scale with scale = amax/448.
+* E4M3 causal prefill -- the causal prefill shapes with Q, K and V all given as
+  E4M3 codes, each tensor with its own amax/448 scale (the same page, What:
+  grouped E4M3 FP32 long-context operator).
 """
 
 from __future__ import annotations
@@ -220,3 +223,33 @@ def verify_inputs(nq: int, context: int, seed: int, hq: int = HQ, hkv: int = HKV
     del kf
     vb = _to_e4m3(vf, v_scale)
     return VerifyInputs(q=q, k_bytes=kb, v_bytes=vb, k_scale=float(k_scale), v_scale=float(v_scale))
+
+
+# ------------------------------------------------------- E4M3 causal prefill
+@dataclass
+class E4M3PrefillInputs:
+    q_bytes: np.ndarray  # uint8 [nq, hq, d] E4M3 codes
+    k_bytes: np.ndarray  # uint8 [n_kv, hkv, d]
+    v_bytes: np.ndarray
+    q_scale: float
+    k_scale: float
+    v_scale: float
+    q_pos0: int
+    scale: float = SCALE
+
+
+def e4m3_prefill_inputs(nq: int, n_kv: int, seed: int, hq: int = HQ, hkv: int = HKV, d: int = D) -> E4M3PrefillInputs:
+    """Causal prefill inputs with Q, K and V all as E4M3 codes: N(0,1) float32
+    draws in the order Q, K, V, each tensor quantised with its own scale
+    amax/448 (the verifier-tail recipe applied to Q as well); the nq query rows
+    sit at the last positions of the n_kv keys."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for shape in ((nq, hq, d), (n_kv, hkv, d), (n_kv, hkv, d)):
+        x = rng.standard_normal(shape, dtype=np.float32)
+        s = np.float32(np.abs(x).max() / np.float32(E4M3_MAX))
+        out.append((_to_e4m3(x, s), float(s)))
+        del x
+    (qb, qs), (kb, ks), (vb, vs) = out
+    return E4M3PrefillInputs(q_bytes=qb, k_bytes=kb, v_bytes=vb, q_scale=qs, k_scale=ks, v_scale=vs,
+                             q_pos0=n_kv - nq)
