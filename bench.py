@@ -142,9 +142,11 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
     family = {"prefill_causal_fwd": "prefill", "prefill_merge": "prefill",
               "paged_prepass": "paged", "paged_fwd": "paged", "paged_merge": "paged",
               "verify_fwd": "verify", "verify_merge": "verify",
-              "prefill_varlen_prepass": "varlen", "prefill_causal_varlen": "varlen", "prefill_merge_varlen": "varlen"}
-    first = {"prefill_causal_fwd", "paged_prepass", "verify_fwd", "prefill_varlen_prepass"}  # a step starts here
-    labels = {"prefill": [prefill_workload(n_kv)], "varlen": [varlen_workload()],
+              "prefill_varlen_prepass": "varlen", "prefill_causal_varlen": "varlen", "prefill_merge_varlen": "varlen",
+              "prefill_causal_e4m3": "e4m3"}
+    first = {"prefill_causal_fwd", "paged_prepass", "verify_fwd", "prefill_varlen_prepass",
+             "prefill_causal_e4m3"}  # a step starts here
+    labels = {"prefill": [prefill_workload(n_kv)], "varlen": [varlen_workload()], "e4m3": [e4m3_workload(128000)],
               "paged": [paged_workload(s) for s in PAGED_SELECTIONS] + [paged_dense_workload(p) for p in PAGED_DENSE_PAGES],
               "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
     true_kib = calib_mib * 1024.0
@@ -366,6 +368,47 @@ def bench_varlen(steps, warmup, seed=0):
     }
 
 
+PEAK_F8_TFLOPS = 2 * PEAK_F16_TFLOPS  # dense fp8 matrix-core peak (5.0 PFLOP/s)
+# Q K^T (half the FLOPs) on the fp8 matrix cores, P V (the other half) on the fp16 ones
+PEAK_E4M3_PREFILL_TFLOPS = 1.0 / (0.5 / PEAK_F8_TFLOPS + 0.5 / PEAK_F16_TFLOPS)
+
+
+def e4m3_workload(n_kv: int) -> str:
+    return f"e4m3_gqa_prefill_q8000_kv{n_kv}"
+
+
+def bench_e4m3(steps, warmup, n_kv=128000, seed=0):
+    """Causal prefill over E4M3 Q/K/V (per-tensor scales) at Q=8000, with Q K^T on the fp8 matrix cores."""
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    nq = 8000
+    x = workloads.e4m3_prefill_inputs(nq, n_kv, seed)
+    q8, k8, v8 = (torch.from_numpy(a).cuda() for a in (x.q_bytes, x.k_bytes, x.v_bytes))
+    o = torch.empty((nq, 6, 256), dtype=torch.float16, device="cuda")
+    ws = torch.empty(max(1, g.gqa_prefill_causal_workspace_size(nq, n_kv, x.q_pos0)), dtype=torch.uint8, device="cuda")
+
+    def step():
+        g.gqa_prefill_causal_e4m3(q8, x.q_scale, k8, x.k_scale, v8, x.v_scale, x.q_pos0, x.scale, o=o, workspace=ws)
+
+    ms, kms = time_steps(step, steps, warmup)
+    flops = prefill_flops(nq, n_kv, x.q_pos0)
+    tf = flops / (kms * 1e-3) / 1e12
+    return {
+        "workload": e4m3_workload(n_kv),
+        "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "roofline": {"kernel": "prefill_causal_e4m3", "bound": "mfma", "achieved": round(tf, 2),
+                     "peak": round(PEAK_E4M3_PREFILL_TFLOPS, 1), "unit": "TFLOP/s",
+                     "frac": round(tf / PEAK_E4M3_PREFILL_TFLOPS, 4),
+                     "peak_note": "Q K^T at the fp8 peak, P V at the fp16 peak",
+                     "frac_of_fp16_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                     "algorithmic_bytes": nq * 6 * 256 + 2 * n_kv * 256 + 2 * nq * 6 * 256,
+                     "traffic": recorded_traffic().get(("prefill_causal_e4m3", e4m3_workload(n_kv)))},
+    }
+
+
 def bench_verify(nq, steps, warmup, copies=3, seed=0):
     import torch
 
@@ -483,6 +526,7 @@ def main(argv=None):
             "paged_dense": [bench_paged(None, args.steps, args.warmup, dense_page_size=ps) for ps in PAGED_DENSE_PAGES],
             "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in VERIFY_QUERIES],
             "varlen": [bench_varlen(args.steps, args.warmup)],
+            "e4m3_prefill": [bench_e4m3(args.steps, args.warmup)],
         }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline_prefill(cfg, r["host"], args.cpu_seconds)

@@ -31,6 +31,8 @@ SIGNATURES = {
     "gqa_prefill_paged_sparse_dropped": (_i32, [_vp, _i32p, _vp]),
     "gqa_verify_fp8kv_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _szp]),
     "gqa_verify_fp8kv": (_i32, [_vp, _vp, _vp, _f32, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gqa_prefill_causal_e4m3": (_i32, [_vp, _f32, _vp, _f32, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
+                                       _vp, _sz, _vp]),
     "gqa_prefill_causal_varlen_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
     "gqa_prefill_causal_varlen": (_i32, [_vp, _vp, _vp, _vp, _vp, _vp, _vp, _i32, _i32, _i32, _i32, _i32, _i32,
                                          ctypes.c_float, _vp, ctypes.c_size_t, _vp]),
@@ -138,6 +140,29 @@ def gqa_prefill_causal(q, k, v, q_pos0: int, scale: float, o=None, workspace=Non
                                   d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
                                   _stream(stream))
     _check(st, "gqa_prefill_causal")
+    return o
+
+
+def gqa_prefill_causal_e4m3(q8, q_scale: float, k8, k_scale: float, v8, v_scale: float, q_pos0: int, scale: float,
+                            o=None, workspace=None, stream=None):
+    """Causal prefill over E4M3 codes; q8 [nq, Hq, D], k8/v8 [n_kv, Hkv, D] uint8 with one fp32 scale each
+    -> o [nq, Hq, D] fp16."""
+    import torch
+
+    nq, hq, d = q8.shape
+    n_kv, hkv, _ = k8.shape
+    if tuple(v8.shape) != tuple(k8.shape):
+        raise ValueError("k and v must have the same shape")
+    if o is None:
+        o = torch.empty((nq, hq, d), dtype=torch.float16, device=q8.device)
+    nbytes = gqa_prefill_causal_workspace_size(nq, n_kv, q_pos0, hq, hkv, d)
+    ws, ws_bytes = _workspace(nbytes, q8.device, workspace)
+    st = lib().gqa_prefill_causal_e4m3(_dev(q8, torch.uint8, "q"), q_scale, _dev(k8, torch.uint8, "k"), k_scale,
+                                       _dev(v8, torch.uint8, "v"), v_scale, _dev(o, torch.float16, "o"), nq, n_kv,
+                                       q_pos0, hq, hkv, d, scale,
+                                       None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+                                       _stream(stream))
+    _check(st, "gqa_prefill_causal_e4m3")
     return o
 
 

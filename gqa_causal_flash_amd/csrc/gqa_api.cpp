@@ -189,6 +189,22 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
                                                (hipStream_t)stream));
 }
 
+// ------------------------------------------------------- E4M3 causal prefill
+gqa_status gqa_prefill_causal_e4m3(const uint8_t* q_e4m3, float q_scale, const uint8_t* k_e4m3, float k_scale,
+                                   const uint8_t* v_e4m3, float v_scale, void* o, int32_t nq, int32_t n_kv,
+                                   int32_t q_pos0, int32_t hq, int32_t hkv, int32_t d, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream) {
+  if (!q_e4m3 || !k_e4m3 || !v_e4m3 || !o) return GQA_ERR_INVALID;
+  if (!good_scale(scale) || !good_scale(q_scale) || !good_scale(k_scale) || !good_scale(v_scale))
+    return GQA_ERR_INVALID;
+  size_t need = 0;
+  gqa_status st = gqa_prefill_causal_workspace_size(nq, n_kv, q_pos0, hq, hkv, d, &need);
+  if (st != GQA_OK) return st;
+  if (need > 0 && (!workspace || workspace_bytes < need)) return GQA_ERR_WORKSPACE;
+  return hip_status(gqa::launch_prefill_causal_e4m3(q_e4m3, q_scale, k_e4m3, k_scale, v_e4m3, v_scale, o, nq, n_kv,
+                                                    q_pos0, hq, scale, workspace, (hipStream_t)stream));
+}
+
 // ------------------------------------------------------------ varlen prefill
 namespace {
 constexpr int32_t kMaxBatch = 1 << 20;

@@ -20,6 +20,10 @@ unsigned long long* prof_clock();
 hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, void* o, int nq, int n_kv, int q_pos0,
                                  int hq, float scale, void* workspace, hipStream_t stream);
 
+hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* k, float k_scale, const void* v,
+                                      float v_scale, void* o, int nq, int n_kv, int q_pos0, int hq, float scale,
+                                      void* workspace, hipStream_t stream);
+
 hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void* v, void* o, float* lse,
                                         const int32_t* cu_q, const int32_t* cu_kv, int batch, int total_q,
                                         int total_kv, float scale, void* workspace, hipStream_t stream);

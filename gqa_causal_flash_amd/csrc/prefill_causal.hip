@@ -52,7 +52,8 @@ struct PrefillParams {
   float* lse;               // per packed row log-sum-exp (natural log), or null
   const int* vdesc;         // varlen: block descriptors (see prefill_varlen_prepass), else null
   uint32_t part_bytes;
-  float c;  // scale * log2(e): scores are kept in log2 units
+  float c;     // scale * log2(e): scores are kept in log2 units
+  float post;  // factor applied to O at the end (the V scale of E4M3 inputs, else 1)
 };
 
 constexpr float kLn2 = 0.69314718055994531f;
@@ -216,14 +217,10 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
   }
 }
 
-template <int C, int W>
-__device__ __forceinline__ void prefill_run(const PrefillParams& p, char* smem, int b, int lo, int hi, bool full,
-                                            int slot) {
-  prefill_piece<C, W>(p, smem, b, lo, hi, full, slot);
-}
-
-template <int C, int W>
-__device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, char* smem) {
+// Runs the pieces of workgroup blockIdx.x: run(b, tile_lo, tile_hi, full, slot)
+// for each (q-block, key range) the schedule gives it.
+template <class Run>
+__device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, Run run) {
   const int w = blockIdx.x;
   if (p.split > 0) {
     // q-blocks are dispatched last first: they are the longest, so the
@@ -232,7 +229,7 @@ __device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, char* 
     const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
     const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
     // the split never exceeds the shortest q-block's tile count, so lo < hi
-    prefill_run<C, W>(p, smem, b, lo, hi, p.split == 1, b * p.split + j);
+    run(b, lo, hi, p.split == 1, b * p.split + j);
     return;
   }
   long long t0 = prefill_range_start(w, p.total, p.grid);
@@ -250,7 +247,7 @@ __device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, char* 
     const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
     const long long seg_end = cb + nt < t1 ? cb + nt : t1;
     const int lo = (int)(t0 - cb), hi = (int)(seg_end - cb);
-    prefill_run<C, W>(p, smem, b, lo, hi, lo == 0 && hi == nt, w + b);
+    run(b, lo, hi, lo == 0 && hi == nt, w + b);
     t0 = seg_end;
     cb += nt;
     ++b;
@@ -269,7 +266,9 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p)
     c0 = clock64();
     r0 = wall_clock64();
   }
-  prefill_workgroup<C, W>(p, smem);
+  prefill_workgroup(p, [&](int b, int lo, int hi, bool full, int slot) {
+    prefill_piece<C, W>(p, smem, b, lo, hi, full, slot);
+  });
   if (stamp) {
     const unsigned long long dc = clock64() - c0, dr = wall_clock64() - r0;
     if (threadIdx.x == 0) {
@@ -277,6 +276,223 @@ __global__ __launch_bounds__(64 * W, 1) void prefill_causal_fwd(PrefillParams p)
       atomicAdd(p.clk + 1, dr);
     }
   }
+}
+
+// ------------------------------------------------------------ E4M3 inputs
+// Causal prefill with Q, K and V given as OCP E4M3 codes and one fp32 scale
+// per tensor (the long-context page's grouped E4M3 operator, "[Perf] Ship the
+// qualified SM70 long-context layout...", What, with Q quantised as well so
+// that S^T = K Q^T runs on the FP8 matrix cores).  Same workgroup shape,
+// schedule, softmax and P V step as the fp16 kernel; what differs:
+//   * Q stays as E4M3 in registers: for product step si (head-dim columns
+//     64si .. 64si+63) lane (row l%32, half h) holds the 32 bytes of columns
+//     64si + 32h .. +31.  K fragments carry the same columns of a key, so the
+//     v_mfma_f32_32x32x64_f8f6f4 sums run over all 64 columns in either
+//     operand's order (every E4M3 product is exact in fp32).
+//   * K tiles stream HBM -> LDS as E4M3 (64 keys x 256 B), chunk c of row r
+//     stored at c ^ (r % 16), so the two 16-byte reads of a fragment are
+//     bank-conflict free.
+//   * V tiles are loaded into registers one tile ahead, decoded exactly to
+//     fp16 (v_cvt_scalef32_pk_f16_fp8) and written into the fp16 V layout of
+//     the next buffer before the step's barrier; P V is the fp16 step.
+//   * q_scale * k_scale joins the softmax scale; v_scale multiplies O at the
+//     end (and the partials before they are stored).
+constexpr int kRowBytes8 = kHeadDim;                 // one E4M3 row: 256 B = 16 chunks
+constexpr int kTileBytes8 = kTileKeys * kRowBytes8;  // 16 KiB
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+
+__device__ __forceinline__ f16x mfma_fp8(v8i a, v8i b, f16x c) {
+  // format 0 = E4M3 for both operands; zero scale operands select the unscaled product
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+__device__ __forceinline__ v8i cat_u4(u4 a, u4 b) {
+  return v8i{(int)a[0], (int)a[1], (int)a[2], (int)a[3], (int)b[0], (int)b[1], (int)b[2], (int)b[3]};
+}
+
+// 16 E4M3 codes -> 16 fp16 values (exact), as two 16-byte chunks.
+__device__ __forceinline__ void decode16(u4 raw, u4& lo, u4& hi) {
+  h2 x[8];
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    x[2 * w] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[w], 1.0f, false);
+    x[2 * w + 1] = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(raw[w], 1.0f, true);
+  }
+  lo = u4{__builtin_bit_cast(unsigned, x[0]), __builtin_bit_cast(unsigned, x[1]), __builtin_bit_cast(unsigned, x[2]),
+          __builtin_bit_cast(unsigned, x[3])};
+  hi = u4{__builtin_bit_cast(unsigned, x[4]), __builtin_bit_cast(unsigned, x[5]), __builtin_bit_cast(unsigned, x[6]),
+          __builtin_bit_cast(unsigned, x[7])};
+}
+
+// Stage K keys tile*64 .. +63 (E4M3) into LDS: wave w copies rows 8w .. 8w+7 as
+// two 1 KiB copies of four rows; lane i of copy j fills physical chunk i%16 of
+// row r = 8w + 4j + i/16 with logical chunk (i%16) ^ (r%16).
+__device__ __forceinline__ void issue_k8(rsrc_t rk, int tile, GQA_LDS char* kdst, int wave, int lane) {
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int r = 8 * wave + 4 * j + (lane >> 4);
+    const uint32_t voff = (uint32_t)r * kRowBytes8 + 16u * (uint32_t)((lane & 15) ^ (r & 15));
+    load_lds_16B(rk, kdst + (8 * wave + 4 * j) * kRowBytes8, voff, (uint32_t)tile * kTileBytes8);
+  }
+}
+
+// V keys tile*64 .. +63 (E4M3): thread t holds 32 codes of key t/8, columns
+// 32(t%8) .. +31.
+__device__ __forceinline__ void load_v8(rsrc_t rv, int tile, int tid, u4 (&raw)[2]) {
+  const uint32_t off = (uint32_t)tile * kTileBytes8 + (uint32_t)(tid >> 3) * kRowBytes8 + 32u * (uint32_t)(tid & 7);
+  raw[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
+  raw[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + 16, 0, 0);
+}
+
+// Decoded V of thread t into the fp16 tile: row r = t/8, logical fp16 chunks
+// 4(t%8) .. +3, each at its swizzled place c ^ 4(r%8).
+__device__ __forceinline__ void store_v16(GQA_LDS char* vdst, int tid, const u4 (&raw)[2]) {
+  const int r = tid >> 3, c0 = 4 * (tid & 7);
+  u4 d[4];
+  decode16(raw[0], d[0], d[1]);
+  decode16(raw[1], d[2], d[3]);
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    *(GQA_LDS u4*)(vdst + r * kRowBytes + 16 * v_phys_chunk(c0 + j, r)) = d[j];
+}
+
+// K fragment of product step si for keys 32kb .. 32kb+31 of the E4M3 tile:
+// lane (key r = l%32, half h) reads logical chunks 4si + 2h and 4si + 2h + 1 of
+// row 32kb + r, at byte 8192kb + (b8 ^ 64si) and that ^ 16, where
+// b8 = 256 r + 16 (2h ^ (r % 16)).
+__device__ __forceinline__ uint32_t k8_lane_base(int lane) {
+  const int r = lane & 31, h = lane >> 5;
+  return 256u * (uint32_t)r + 16u * (uint32_t)((2 * h) ^ (r & 15));
+}
+__device__ __forceinline__ v8i read_k8_frag(const GQA_LDS char* kt, uint32_t bk, int kb, int si) {
+  const uint32_t a = (bk ^ (64u * si)) + 8192u * kb;
+  const u4 x = *(const GQA_LDS u4*)(kt + a);
+  const u4 y = *(const GQA_LDS u4*)(kt + (a ^ 16u));
+  return cat_u4(x, y);
+}
+
+// LDS of the E4M3 kernel: two fp16 V tiles and two E4M3 K tiles, each its own
+// array so that the compiler can tell the tile being read from the one being
+// loaded (it would otherwise wait for the next tile's loads before every read).
+struct E4M3Lds {
+  GQA_LDS char* v16[2];
+  GQA_LDS char* k8[2];
+};
+
+template <int W>
+__device__ __forceinline__ void prefill_piece_e4m3(const PrefillParams& p, const E4M3Lds& sm, int b, int tile_lo,
+                                                   int tile_hi, bool full, int slot) {
+  constexpr int kRowsPerWave = 32;
+  static_assert(kRowsPerWave * W == kRowsPerBlock && W == 8, "eight waves of 32 rows");
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int half = lane >> 5;
+  const int col = lane & 31;
+
+  const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes8);
+  const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes8);
+  const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes8);
+
+  const int row_base = b * kRowsPerBlock + wave * kRowsPerWave;
+  const bool wave_active = row_base < p.nrows;
+  const int wrow_hi = min(row_base + kRowsPerWave - 1, p.nrows - 1);
+  const int wpos_lo = p.q_pos0 + row_base / kGroup;
+  const int wpos_hi = p.q_pos0 + wrow_hi / kGroup;
+
+  const int row = row_base + col;
+  const int pos = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
+  v8i qf[4];
+  {
+    const uint32_t qoff = (uint32_t)row * kRowBytes8 + 32u * half;
+#pragma unroll
+    for (int si = 0; si < 4; ++si)
+      qf[si] = cat_u4(__builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * si, 0, 0),
+                      __builtin_amdgcn_raw_buffer_load_b128(rq, qoff + 64 * si + 16, 0, 0));
+  }
+
+  f16x acc[1][8];
+#pragma unroll
+  for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
+  float m[1] = {-INFINITY}, l[1] = {0.f};
+
+  uint32_t bk = k8_lane_base(lane);
+  uint32_t bv = v_lane_base(lane);
+
+  // first tile: K into buffer 0, V decoded into fp16 buffer 0
+  {
+    issue_k8(rk, tile_lo, sm.k8[0], wave, lane);
+    u4 raw[2];
+    load_v8(rv, tile_lo, tid, raw);
+    store_v16(sm.v16[0], tid, raw);
+    wait_vmem();
+    __syncthreads();
+  }
+
+  auto step = [&](auto bufc, int tile) {
+    constexpr int BUF = decltype(bufc)::value;
+    const bool more = tile + 1 < tile_hi;
+    u4 raw[2];
+    if (more) {
+      issue_k8(rk, tile + 1, sm.k8[BUF ^ 1], wave, lane);
+      load_v8(rv, tile + 1, tid, raw);
+    }
+    const GQA_LDS char* kt = sm.k8[BUF];
+    const GQA_LDS char* vt = sm.v16[BUF];
+
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int k0 = tile * kTileKeys + 32 * kb;
+      if (!wave_active || k0 > wpos_hi) continue;  // every key of this block is in the future
+      asm volatile("" : "+v"(bk), "+v"(bv));
+      f16x sc[1];
+      sc[0] = f16x{};
+      v8i kf0 = read_k8_frag(kt, bk, kb, 0);
+      v8i kf1 = read_k8_frag(kt, bk, kb, 1);
+      sc[0] = mfma_fp8(kf0, qf[0], sc[0]);
+      kf0 = read_k8_frag(kt, bk, kb, 2);
+      sc[0] = mfma_fp8(kf1, qf[1], sc[0]);
+      kf1 = read_k8_frag(kt, bk, kb, 3);
+      sc[0] = mfma_fp8(kf0, qf[2], sc[0]);
+      sc[0] = mfma_fp8(kf1, qf[3], sc[0]);
+      h8 pk[1][2];
+      softmax_32keys<1>(sc, acc, m, l, p.c, k0 + 31 > wpos_lo,
+                        [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; }, pk);
+      pv_32keys<1>(vt, bv, kb, pk, acc);  // O^T += V^T P^T
+    }
+    if (more) store_v16(sm.v16[BUF ^ 1], tid, raw);
+    wait_vmem();
+    __syncthreads();
+  };
+
+  for (int tile = tile_lo; tile < tile_hi; tile += 2) {
+    step(std::integral_constant<int, 0>{}, tile);
+    if (tile + 1 < tile_hi) step(std::integral_constant<int, 1>{}, tile + 1);
+  }
+
+  const float lt = swap_halves_sum(l[0]);
+  if (full) {
+    const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+    store_rows_f16(ro, row, half, acc[0], lt, p.post);
+  } else {
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[0][dt] *= p.post;
+    const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+    store_partial(rp, (uint32_t)slot * (uint32_t)(kPartialFloats * 4), kRowsPerBlock, wave * kRowsPerWave + col, half,
+                  acc[0], m[0], lt);
+  }
+}
+
+__global__ __launch_bounds__(512, 1) void prefill_causal_e4m3(PrefillParams p) {
+  __shared__ __attribute__((aligned(1024))) char v16a[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char v16b[kTileBytes];
+  __shared__ __attribute__((aligned(1024))) char k8a[kTileBytes8];
+  __shared__ __attribute__((aligned(1024))) char k8b[kTileBytes8];
+  const E4M3Lds sm = {{(GQA_LDS char*)v16a, (GQA_LDS char*)v16b}, {(GQA_LDS char*)k8a, (GQA_LDS char*)k8b}};
+  prefill_workgroup(p, [&](int b, int lo, int hi, bool full, int slot) {
+    prefill_piece_e4m3<8>(p, sm, b, lo, hi, full, slot);
+  });
 }
 
 // Exact merge of the partials of q-blocks that were split across workgroups:
@@ -502,11 +718,48 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.split = s.split;
   p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
   p.c = scale * kLog2e;
+  p.post = 1.0f;
   p.clk = prof_clock();
   p.lse = nullptr;
   p.vdesc = nullptr;
   prof_before(stream);
   hipLaunchKernelGGL((prefill_causal_fwd<kPrefillC, kPrefillW>), dim3(s.grid), dim3(64 * kPrefillW), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  prof_after(stream);
+  if (e != hipSuccess) return e;
+  if (prefill_needs_merge(s)) {
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / 64)), dim3(256), 0, stream, p);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* k, float k_scale, const void* v,
+                                      float v_scale, void* o, int nq, int n_kv, int q_pos0, int hq, float scale,
+                                      void* workspace, hipStream_t stream) {
+  const PrefillSched s = prefill_schedule(nq, hq, q_pos0);
+  PrefillParams p;
+  p.q = (const _Float16*)q;  // E4M3 codes, read as bytes
+  p.k = (const _Float16*)k;
+  p.v = (const _Float16*)v;
+  p.o = (_Float16*)o;
+  p.part = (float*)workspace;
+  p.total = s.total;
+  p.nrows = s.nrows;
+  p.kv_live = q_pos0 + nq;
+  (void)n_kv;
+  p.q_pos0 = q_pos0;
+  p.nqb = s.nqb;
+  p.grid = s.grid;
+  p.split = s.split;
+  p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
+  p.c = scale * q_scale * k_scale * kLog2e;
+  p.post = v_scale;
+  p.clk = nullptr;
+  p.lse = nullptr;
+  p.vdesc = nullptr;
+  prof_before(stream);
+  hipLaunchKernelGGL(prefill_causal_e4m3, dim3(s.grid), dim3(512), 0, stream, p);
   hipError_t e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess) return e;
@@ -549,6 +802,7 @@ hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void
   p.grid = vs.cap * vs.split;
   p.split = vs.split;
   p.c = scale * kLog2e;
+  p.post = 1.0f;
   p.clk = nullptr;
   p.lse = lse;
   p.vdesc = pre.desc;

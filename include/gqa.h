@@ -82,6 +82,30 @@ gqa_status gqa_prefill_causal(const void* q, const void* k, const void* v, void*
                               size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ *
+ * Causal prefill over E4M3 inputs.
+ *
+ * The long-context page ("[Perf] Ship the qualified SM70 long-context layout
+ * and drop its context fences", What) runs its grouped operator over a K/V
+ * cache kept as E4M3 codes with FP32 arithmetic.  Here Q is quantised the same
+ * way so that the Q K^T products run on the FP8 matrix cores: the operation is
+ * the causal prefill of gqa_prefill_causal applied to the decoded values
+ *     Q = decode(q_e4m3) * q_scale,  K = decode(k_e4m3) * k_scale,
+ *     V = decode(v_e4m3) * v_scale,
+ * with decode the OCP E4M3 ("E4M3FN") format and one fp32 scale per tensor.
+ *
+ *   q_e4m3 [nq][hq][d] uint8, k_e4m3 / v_e4m3 [n_kv][hkv][d] uint8 (device)
+ *   o      [nq][hq][d] fp16 (device), query row r at position q_pos0 + r
+ *   scales finite and > 0; the workspace is the one gqa_prefill_causal needs
+ *   (same query, gqa_prefill_causal_workspace_size), same shape family and
+ *   errors.  Every E4M3 product is exact in fp32; P is rounded to fp16 and
+ *   P V accumulates in fp32, as in gqa_prefill_causal.
+ * ------------------------------------------------------------------------ */
+gqa_status gqa_prefill_causal_e4m3(const uint8_t* q_e4m3, float q_scale, const uint8_t* k_e4m3, float k_scale,
+                                   const uint8_t* v_e4m3, float v_scale, void* o, int32_t nq, int32_t n_kv,
+                                   int32_t q_pos0, int32_t hq, int32_t hkv, int32_t d, float scale, void* workspace,
+                                   size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
  * Varlen causal prefill: a batch of independent sequences packed end to end.
  *
  * The dense causal prefill above, applied to each sequence of a batch the

@@ -187,3 +187,28 @@ def test_varlen_workspace_query():
     assert n.value > 0
     assert g.lib().gqa_prefill_causal_varlen_workspace_size(0, 10, 6, 1, 256, ctypes.byref(n)) == g.GQA_ERR_INVALID
     assert g.lib().gqa_prefill_causal_varlen_skipped(None, ctypes.byref(ctypes.c_int32()), None) == g.GQA_ERR_INVALID
+
+
+def _e4m3(**kw):
+    a = dict(q=FAKE, qs=0.01, k=FAKE, ks=0.01, v=FAKE, vs=0.01, o=FAKE, nq=8000, n_kv=128000, q_pos0=120000, hq=6,
+             hkv=1, d=256, scale=0.0625, ws=None, ws_bytes=0)
+    a.update(kw)
+    return g.lib().gqa_prefill_causal_e4m3(a["q"], a["qs"], a["k"], a["ks"], a["v"], a["vs"], a["o"], a["nq"],
+                                           a["n_kv"], a["q_pos0"], a["hq"], a["hkv"], a["d"], a["scale"], a["ws"],
+                                           a["ws_bytes"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(q=None), g.GQA_ERR_INVALID),
+    (dict(v=None), g.GQA_ERR_INVALID),
+    (dict(qs=0.0), g.GQA_ERR_INVALID),
+    (dict(ks=float("nan")), g.GQA_ERR_INVALID),
+    (dict(vs=-1.0), g.GQA_ERR_INVALID),
+    (dict(q_pos0=120001), g.GQA_ERR_INVALID),
+    (dict(hq=8), g.GQA_ERR_UNSUPPORTED),
+    (dict(d=128), g.GQA_ERR_UNSUPPORTED),
+    (dict(), g.GQA_ERR_WORKSPACE),
+    (dict(ws=FAKE, ws_bytes=1024), g.GQA_ERR_WORKSPACE),
+])
+def test_e4m3_prefill_rejects_before_launch(kw, status):
+    assert _e4m3(**kw) == status
