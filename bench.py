@@ -62,7 +62,7 @@ PAGE_MS_Q8000_KV128000 = 100.20284
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_per_launch.md")
 PAGED_SELECTIONS = (64, 512, 2048)
 PAGED_DENSE_PAGES = (16, 784)  # paged dense causal prefill: every block up to the diagonal selected
-VERIFY_QUERIES = (2, 4, 8)
+VERIFY_QUERIES = (1, 2, 4, 8)  # 1: the single-row tail
 
 
 def prefill_workload(n_kv: int) -> str:

@@ -24,7 +24,7 @@ def test_summarize_counters_scales_and_assigns_workloads(tmp_path, monkeypatch):
     fetch = [(copy, 512.0)] * 3 + [(_k("prefill_causal_fwd"), 100.0), (_k("prefill_merge"), 10.0)] * 2
     for s in range(3):
         fetch += [(_k("paged_prepass"), 1.0), (_k("paged_fwd"), 20.0 + s)] * 2
-    for q in range(3):
+    for q in range(len(bench.VERIFY_QUERIES)):
         fetch += [(_k("verify_fwd"), 30.0 + q), (_k("verify_merge"), 3.0)] * 2
     write = [(n, 2 * v if n == copy else v / 2) for n, v in fetch]
     _write_counters(tmp_path / "f.csv", "FETCH_SIZE", fetch)

@@ -130,3 +130,26 @@ def test_graph_prefill_causal_varlen():
         return g.gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, x.scale)[0].clone()
 
     _replay_matches(graph, out, eager, refresh)
+
+
+def test_graph_prefill_causal_e4m3():
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    nq, n_kv = 512, 9000
+    x = workloads.e4m3_prefill_inputs(nq, n_kv, seed=22)
+    q8, k8, v8 = (torch.from_numpy(a).cuda() for a in (x.q_bytes, x.k_bytes, x.v_bytes))
+    ws = torch.empty(max(1, g.gqa_prefill_causal_workspace_size(nq, n_kv, x.q_pos0)), dtype=torch.uint8,
+                     device="cuda")
+    out = torch.empty((nq, 6, 256), dtype=torch.float16, device="cuda")
+    call = lambda **kw: g.gqa_prefill_causal_e4m3(q8, x.q_scale, k8, x.k_scale, v8, x.v_scale, x.q_pos0, x.scale,
+                                                  **kw)
+    eager = call().clone()
+    graph = _capture(lambda: call(o=out, workspace=ws))
+
+    def refresh():
+        k8.copy_(torch.from_numpy(workloads.e4m3_prefill_inputs(nq, n_kv, seed=23).k_bytes))
+        return call()
+
+    _replay_matches(graph, out, eager, refresh)

@@ -21,9 +21,10 @@ def _oracle(x):
     return oracle.verify_fp8kv(x.q, x.k_bytes, x.v_bytes, x.k_scale, x.v_scale, x.scale)[0]
 
 
-@pytest.mark.parametrize("nq", [2, 4, 8])
+@pytest.mark.parametrize("nq", [1, 2, 4, 8])
 def test_verify_parity_full_context(nq):
-    """Verifier tail of 2/4/8 rows at context 261888 (E4M3 K/V, per-tensor scales)."""
+    """Verifier tail of 1 (the single-row tail) and 2/4/8 rows at context 261888 (E4M3 K/V,
+    per-tensor scales)."""
     x = workloads.verify_inputs(nq, workloads.VERIFY_CONTEXT, seed=nq)
     assert_parity(_gpu(x), _oracle(x), f"q={nq} ctx=261888")
 
