@@ -82,6 +82,10 @@ struct RawRing {
   char* s[kRing];
 };
 
+// PAIR (at most 32 packed rows): both waves hold all the rows and compute
+// alternate tiles, each leaving its own partial; otherwise wave c holds rows
+// 32c .. 32c+31 and both compute every tile.
+template <bool PAIR>
 __global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
   __shared__ __attribute__((aligned(1024))) char r0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char r1[kSlotBytes];
@@ -117,8 +121,8 @@ __global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
     for (int i = 0; i < 8; ++i) load_lds_16B(rkv, dst + i * 1024, loff[i], (uint32_t)t * kRawTile);
   };
 
-  const int row = 32 * wave + col;
-  const bool rows_active = 32 * wave < p.nrows;
+  const int row = (PAIR ? 0 : 32 * wave) + col;
+  const bool rows_active = PAIR || 32 * wave < p.nrows;
   const int pos = (p.n_kv - p.nq) + min(row, p.nrows - 1) / kGroup;
   const int pos_min = p.n_kv - p.nq;  // first query position
   // Q as B fragments in the permuted column order: step s, lane half h holds
@@ -150,132 +154,210 @@ __global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
   const uint32_t vswz = v_swz(vrow0);                                 // (16t keeps the swizzle)
   uint32_t vbase = (uint32_t)vrow0 * kFp8Row + 8u * (sk & 1);
 
-  // prologue: kRing - 1 tiles in flight, tile j in slot j
+  // one 32-key tile t from the raw K bytes at kt (V bytes follow)
+  auto compute = [&](const GQA_LDS char* kt, int t) {
+    const GQA_LDS char* vt = kt + kRawTile;
+    const int k0 = t * kVTileKeys;
+    asm volatile("" : "+v"(kbase), "+v"(vbase));
+    // S^T = K Q^T
+    f16x s1[1];
+    s1[0] = f16x{};
 #pragma unroll
-  for (int j = 0; j < kRing - 1; ++j)
-    if (j < n) issue(ring.s[j], t_lo + j);
-
-  // iteration it computes tile t_lo + it from slot it % kRing
-  auto step = [&](auto slotc, int it) {
-    constexpr int SL = decltype(slotc)::value;
-    const int t = t_lo + it;
-    // tile t has landed once at most min(n - 1 - it, kRing - 2) later tiles are outstanding
-    const int later = min(n - 1 - it, kRing - 2);
-    if (later >= 3)
-      asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-    else if (later == 2)
-      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-    else if (later == 1)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    lds_barrier();  // both halves of tile t are in; the slot of tile t-1 is free
-    if (it + kRing - 1 < n) issue(ring.s[(SL + kRing - 1) % kRing], t + kRing - 1);
-    if (rows_active) {
-      const GQA_LDS char* kt = (const GQA_LDS char*)ring.s[SL];
-      const GQA_LDS char* vt = kt + kRawTile;
-      const int k0 = t * kVTileKeys;
-      asm volatile("" : "+v"(kbase), "+v"(vbase));
-      // S^T = K Q^T
-      f16x s1[1];
-      s1[0] = f16x{};
+    for (int si = 0; si < 16; ++si) {
+      const uint32_t ch = (uint32_t)(8 * half + (si >> 1)) ^ k_swz(col);
+      const v2i raw = *(const GQA_LDS v2i*)(kt + kbase + 16u * ch + 8u * (si & 1));
+      s1[0] = mfma(decode8(raw), qf[0][si], s1[0]);
+    }
+    h8 pk[1][2];
+    softmax_32keys<1>(s1, acc, m, l, p.c, k0 + 31 > pos_min,
+                      [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; }, pk);
+    // O^T += V^T P^T
 #pragma unroll
-      for (int si = 0; si < 16; ++si) {
-        const uint32_t ch = (uint32_t)(8 * half + (si >> 1)) ^ k_swz(col);
-        const v2i raw = *(const GQA_LDS v2i*)(kt + kbase + 16u * ch + 8u * (si & 1));
-        s1[0] = mfma(decode8(raw), qf[0][si], s1[0]);
-      }
-      h8 pk[1][2];
-      softmax_32keys<1>(s1, acc, m, l, p.c, k0 + 31 > pos_min,
-                        [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; }, pk);
-      // O^T += V^T P^T
-#pragma unroll
-      for (int st = 0; st < 16; ++st) {
-        const int dt = st >> 1, tt = st & 1;
-        const uint32_t ch = (uint32_t)(2 * dt + (g & 1)) ^ vswz;
-        const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
-            (GQA_LDS v2i*)(vt + vbase + (uint32_t)(16 * tt) * kFp8Row + 16u * ch));
-        acc[0][dt] = mfma(decode8(raw), pk[0][tt], acc[0][dt]);
-      }
+    for (int st = 0; st < 16; ++st) {
+      const int dt = st >> 1, tt = st & 1;
+      const uint32_t ch = (uint32_t)(2 * dt + (g & 1)) ^ vswz;
+      const v2i raw = __builtin_amdgcn_ds_read_tr8_b64_v2i32(
+          (GQA_LDS v2i*)(vt + vbase + (uint32_t)(16 * tt) * kFp8Row + 16u * ch));
+      acc[0][dt] = mfma(decode8(raw), pk[0][tt], acc[0][dt]);
     }
   };
-  for (int it = 0; it < n; it += kRing) {
-    step(std::integral_constant<int, 0>{}, it);
-    if (it + 1 >= n) break;
-    step(std::integral_constant<int, 1>{}, it + 1);
-    if (it + 2 >= n) break;
-    step(std::integral_constant<int, 2>{}, it + 2);
-    if (it + 3 >= n) break;
-    step(std::integral_constant<int, 3>{}, it + 3);
-    if (it + 4 >= n) break;
-    step(std::integral_constant<int, 4>{}, it + 4);
+
+  if constexpr (PAIR) {
+    // double step d takes tiles 2d (wave 0) and 2d + 1 (wave 1) from slot pair
+    // d % 2; the tiles of double step d + 1 load into the other pair meanwhile
+    if (0 < n) issue(ring.s[0], t_lo);
+    if (1 < n) issue(ring.s[1], t_lo + 1);
+    // the loop is written once per wave so that every slot a wave reads is a
+    // compile-time choice (the compiler then knows the reads miss the slots
+    // being loaded)
+    auto run = [&](auto wavec) {
+      constexpr int WV = decltype(wavec)::value;
+      auto dstep = [&](auto pairc, int d) {
+        constexpr int P = decltype(pairc)::value;
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();  // tiles 2d, 2d + 1 are in; the other pair's tiles have been used
+        if (2 * d + 2 < n) issue(ring.s[2 * (P ^ 1)], t_lo + 2 * d + 2);
+        if (2 * d + 3 < n) issue(ring.s[2 * (P ^ 1) + 1], t_lo + 2 * d + 3);
+        if (2 * d + WV < n) compute((const GQA_LDS char*)ring.s[2 * P + WV], t_lo + 2 * d + WV);
+      };
+      for (int d = 0; 2 * d < n; d += 2) {
+        dstep(std::integral_constant<int, 0>{}, d);
+        if (2 * d + 2 >= n) break;
+        dstep(std::integral_constant<int, 1>{}, d + 1);
+      }
+    };
+    if (wave == 0)
+      run(std::integral_constant<int, 0>{});
+    else
+      run(std::integral_constant<int, 1>{});
+  } else {
+    // prologue: kRing - 1 tiles in flight, tile j in slot j
+#pragma unroll
+    for (int j = 0; j < kRing - 1; ++j)
+      if (j < n) issue(ring.s[j], t_lo + j);
+
+    // iteration it computes tile t_lo + it from slot it % kRing
+    auto step = [&](auto slotc, int it) {
+      constexpr int SL = decltype(slotc)::value;
+      const int t = t_lo + it;
+      // tile t has landed once at most min(n - 1 - it, kRing - 2) later tiles are outstanding
+      const int later = min(n - 1 - it, kRing - 2);
+      if (later >= 3)
+        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
+      else if (later == 2)
+        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+      else if (later == 1)
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      lds_barrier();  // both halves of tile t are in; the slot of tile t-1 is free
+      if (it + kRing - 1 < n) issue(ring.s[(SL + kRing - 1) % kRing], t + kRing - 1);
+      if (rows_active) compute((const GQA_LDS char*)ring.s[SL], t);
+    };
+    for (int it = 0; it < n; it += kRing) {
+      step(std::integral_constant<int, 0>{}, it);
+      if (it + 1 >= n) break;
+      step(std::integral_constant<int, 1>{}, it + 1);
+      if (it + 2 >= n) break;
+      step(std::integral_constant<int, 2>{}, it + 2);
+      if (it + 3 >= n) break;
+      step(std::integral_constant<int, 3>{}, it + 3);
+      if (it + 4 >= n) break;
+      step(std::integral_constant<int, 4>{}, it + 4);
+    }
   }
 
+  float lt = swap_halves_sum(l[0]);
+  if constexpr (PAIR) {
+    // wave 1 hands its state to wave 0 through LDS (the ring is idle now): the
+    // two waves hold the same rows in the same lanes, so wave 0 combines
+    // register by register, O = 2^(m1-M) O1 + 2^(m2-M) O2 and likewise l.
+    // Value j of a lane (128 accumulators, m, l) sits in ring slot j / 64 at
+    // float (j % 64) * 64 + lane.
+    auto xv = [&](int j) -> GQA_LDS float& {
+      return ((GQA_LDS float*)ring.s[j >> 6])[(j & 63) * 64 + lane];
+    };
+    lds_barrier();  // every wave is done with the ring
+    if (wave == 1) {
+#pragma unroll
+      for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) xv(16 * dt + v) = acc[0][dt][v];
+      xv(128) = m[0];
+      xv(129) = lt;
+    }
+    lds_barrier();
+    if (wave == 1) return;
+    const float m2 = xv(128), l2 = xv(129);
+    const float mm = fmaxf(m[0], m2);
+    const float a1 = (m[0] == -INFINITY) ? 0.f : fast_exp2(m[0] - mm);
+    const float a2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mm);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[0][dt][v] = a1 * acc[0][dt][v] + a2 * xv(16 * dt + v);
+    m[0] = mm;
+    lt = a1 * lt + a2 * l2;
+  }
   if (rows_active && row < p.nrows) {
+    // partial slot, row-major: acc[64 rows][256 columns], then m[64], l[64];
+    // register 4g .. 4g+3 of tile dt holds columns 32dt + 8g + 4h .. +3
     const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-    store_partial(rp, (uint32_t)blockIdx.x * (uint32_t)(kVerifySlotFloats * 4), kVerifySlotRows, row, half, acc[0],
-                  m[0], swap_halves_sum(l[0]));
+    const uint32_t sb = (uint32_t)blockIdx.x * (uint32_t)(kVerifySlotFloats * 4);
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; ++g4) {
+        const f4 x = {acc[0][dt][4 * g4], acc[0][dt][4 * g4 + 1], acc[0][dt][4 * g4 + 2], acc[0][dt][4 * g4 + 3]};
+        store_16B(rp, sb + (uint32_t)(row * kHeadDim + 32 * dt + 8 * g4 + 4 * half) * 4, __builtin_bit_cast(u4, x));
+      }
+    if (half == 0) {
+      const uint32_t mo = sb + (uint32_t)(kVerifySlotRows * kHeadDim * 4);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(m[0]), rp, mo + row * 4, 0, 0);
+      __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(lt), rp, mo + (kVerifySlotRows + row) * 4, 0, 0);
+    }
   }
 }
 
 // Merge of the workgroups' partials: workgroup (r, part) combines row r,
-// head-dim columns 64*part .. 64*part+63, over all slots in one pass.  Thread
-// (quad, sl) takes columns 64*part + 4*quad .. +3 of the slots sl, sl+32, ...,
-// keeping a running maximum and rescaling its sums when the maximum grows;
-// the 32 slot lanes are then combined the same way through LDS.
+// columns 64 part .. 64 part + 63.  Thread (quad, sl) takes columns
+// 64 part + 4 quad .. +3 of slots sl, sl + 32, ... (all its loads in flight
+// together; the 16 quads of one slot read 256 contiguous bytes), then the
+// maximum of m and the sums of 2^(m_s - M) acc_s and 2^(m_s - M) l_s are
+// taken over the 32 slot lanes through LDS.
 constexpr int kMergeLanes = 32;
+constexpr int kMergeSlots = kVerifyMaxGrid / kMergeLanes;  // slots per thread
+
 __global__ __launch_bounds__(16 * kMergeLanes) void verify_merge(VerifyParams p) {
-  __shared__ float red[kMergeLanes][16][6];
-  const int r = blockIdx.x >> 2;
-  const int part = blockIdx.x & 3;
-  const int tid = threadIdx.x;
-  const int quad = tid & 15;
-  const int sl = tid >> 4;
+  __shared__ float red[kMergeLanes][16][5];
+  __shared__ float rmax[kMergeLanes];
+  const int r = blockIdx.x >> 2, part = blockIdx.x & 3;
+  const int tid = threadIdx.x, quad = tid & 15, sl = tid >> 4;
   const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
   const uint32_t slot_bytes = (uint32_t)(kVerifySlotFloats * 4);
   const uint32_t m_off = (uint32_t)(kVerifySlotRows * kHeadDim * 4);
-  const uint32_t qoff = (uint32_t)(((16 * part + quad) * kVerifySlotRows + r) * 16);
-  float M = -INFINITY, L = 0.f;
-  f4 o = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-  for (int s = sl; s < p.grid; s += kMergeLanes) {
-    const uint32_t sb = s * slot_bytes;
-    const float ms = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + r * 4, 0, 0));
-    const float ls = __uint_as_float(
-        __builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kVerifySlotRows + r) * 4, 0, 0));
-    const f4 x = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rp, sb + qoff, 0, 0));
-    if (ms > M) {  // rescale what was summed so far to the new maximum
-      const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - ms);
-      o *= a;
-      L *= a;
-      M = ms;
-    }
-    const float a = (ms == -INFINITY) ? 0.f : fast_exp2(ms - M);
-    o += a * x;
-    L += a * ls;
+  const uint32_t xoff = (uint32_t)(r * kHeadDim + 64 * part + 4 * quad) * 4;
+  float ms[kMergeSlots], ls[kMergeSlots];
+  f4 xs[kMergeSlots];
+  float M = -INFINITY;
+#pragma unroll
+  for (int i = 0; i < kMergeSlots; ++i) {
+    const int s = sl + kMergeLanes * i;
+    const uint32_t sb = (uint32_t)s * slot_bytes;  // past the workspace for s >= grid: reads as zero
+    const bool ok = s < p.grid;
+    ms[i] = ok ? __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + r * 4, 0, 0)) : -INFINITY;
+    ls[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kVerifySlotRows + r) * 4, 0, 0));
+    xs[i] = __builtin_bit_cast(f4, __builtin_amdgcn_raw_buffer_load_b128(rp, sb + xoff, 0, 0));
+    M = fmaxf(M, ms[i]);
   }
-  red[sl][quad][0] = M;
-  red[sl][quad][1] = L;
-  red[sl][quad][2] = o[0];
-  red[sl][quad][3] = o[1];
-  red[sl][quad][4] = o[2];
-  red[sl][quad][5] = o[3];
+  if (quad == 0) rmax[sl] = M;
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < kMergeLanes; ++i) M = fmaxf(M, rmax[i]);
+  f4 o = {0.f, 0.f, 0.f, 0.f};
+  float L = 0.f;
+#pragma unroll
+  for (int i = 0; i < kMergeSlots; ++i) {
+    const float a = (ms[i] == -INFINITY) ? 0.f : fast_exp2(ms[i] - M);
+    o += a * xs[i];
+    L += a * ls[i];
+  }
+  red[sl][quad][0] = L;
+  red[sl][quad][1] = o[0];
+  red[sl][quad][2] = o[1];
+  red[sl][quad][3] = o[2];
+  red[sl][quad][4] = o[3];
   __syncthreads();
   if (sl == 0) {
-    float Mt = -INFINITY;
-#pragma unroll
-    for (int i = 0; i < kMergeLanes; ++i) Mt = fmaxf(Mt, red[i][quad][0]);
     f4 t = {0.f, 0.f, 0.f, 0.f};
     float lt = 0.f;
 #pragma unroll
     for (int i = 0; i < kMergeLanes; ++i) {
-      const float mi = red[i][quad][0];
-      const float a = (mi == -INFINITY) ? 0.f : fast_exp2(mi - Mt);
-      lt += a * red[i][quad][1];
-      t[0] += a * red[i][quad][2];
-      t[1] += a * red[i][quad][3];
-      t[2] += a * red[i][quad][4];
-      t[3] += a * red[i][quad][5];
+      lt += red[i][quad][0];
+      t[0] += red[i][quad][1];
+      t[1] += red[i][quad][2];
+      t[2] += red[i][quad][3];
+      t[3] += red[i][quad][4];
     }
     const float inv = lt > 0.f ? p.v_scale / lt : 0.f;
     const h2 lo = cvt2(t[0] * inv, t[1] * inv), hi = cvt2(t[2] * inv, t[3] * inv);
@@ -304,7 +386,10 @@ hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v
   p.c = scale * k_scale * kLog2e;
   p.v_scale = v_scale;
   prof_before(stream);
-  hipLaunchKernelGGL(verify_fwd, dim3(s.grid), dim3(128), 0, stream, p);
+  if (s.pair)
+    hipLaunchKernelGGL(verify_fwd<true>, dim3(s.grid), dim3(128), 0, stream, p);
+  else
+    hipLaunchKernelGGL(verify_fwd<false>, dim3(s.grid), dim3(128), 0, stream, p);
   hipError_t e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess) return e;

@@ -20,17 +20,21 @@ constexpr int kVerifyMinTiles = 8;
 struct VerifySched {
   int ntiles;
   int grid;
+  bool pair;  // the two waves of a workgroup split the tiles (and combine before writing)
 };
 
+// With at most 32 packed rows (q <= 5) one 32-row block holds them all, so the
+// workgroup's two waves both hold every row and take alternate tiles instead
+// of one row block each; they combine their states in LDS before the
+// workgroup writes its one partial.
 inline VerifySched verify_schedule(int nq, int n_kv, int hq) {
-  (void)nq;
-  (void)hq;
   VerifySched s;
   s.ntiles = (n_kv + 31) / 32;
   int g = s.ntiles / kVerifyMinTiles;
   if (g < 1) g = 1;
   if (g > kVerifyMaxGrid) g = kVerifyMaxGrid;
   s.grid = g;
+  s.pair = nq * hq <= 32;
   return s;
 }
 
