@@ -11,12 +11,15 @@
 // into the softmax scale and the V scale into the final normalisation.
 //
 // The work is bound by HBM bandwidth (K + V = 512 B per key), so the key range
-// is split evenly over two workgroups per compute unit.  A workgroup (two
-// waves, one per 32-row block of the <= 48 packed query rows) streams its
-// keys in 32-key tiles of raw bytes through a ring of kRing LDS slots with
-// direct HBM -> LDS loads, kRing - 1 tiles ahead of the one it computes, so
-// each compute unit keeps 128 KiB of loads in flight.  The bytes are decoded
-// to fp16 in registers, right where the matrix cores take them:
+// is split evenly over two workgroups per compute unit.  A workgroup of two
+// waves streams its keys in 32-key tiles of raw bytes through a ring of LDS
+// slots with direct HBM -> LDS loads.  With more than 32 packed query rows
+// (q = 6..8) wave c holds rows 32c .. 32c+31 and both compute every tile,
+// kRing - 1 tiles ahead of the loads; with at most 32 (q = 1..5, the
+// single-row tail included) both waves hold all the rows and take alternate
+// tiles, two tiles ahead, and combine their states before the workgroup
+// writes its partial.  The bytes are decoded to fp16 in registers, right
+// where the matrix cores take them:
 //   K fragments (S^T = K Q^T, A operand) by an 8-byte LDS read per lane;
 //     the head-dimension order of the product is permuted so that lane half h
 //     covers columns 128h .. 128h+127 (Q is loaded in the same order);

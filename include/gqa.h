@@ -201,7 +201,8 @@ gqa_status gqa_prefill_paged_sparse_dropped(const void* workspace, int32_t* coun
  * long-context layout...", What and Changes): a grouped attention operator over
  * an E4M3 K/V cache with fp32 accumulation, used for a speculative-decoding
  * verifier tail of query_rows 2..8 at contexts up to the operator capability
- * of 262144 tokens.
+ * of 262144 tokens, and (nq = 1) for the single-row tail the same page routes
+ * to its compact operator.
  *
  *   q        [nq][hq][d] fp16: the last nq positions n_kv-nq .. n_kv-1
  *   k_e4m3, v_e4m3 [n_kv][hkv][d] uint8 OCP E4M3 ("E4M3FN") codes; the cached
