@@ -393,6 +393,7 @@ def bench_e4m3(steps, warmup, n_kv=128000, seed=0):
         g.gqa_prefill_causal_e4m3(q8, x.q_scale, k8, x.k_scale, v8, x.v_scale, x.q_pos0, x.scale, o=o, workspace=ws)
 
     ms, kms = time_steps(step, steps, warmup)
+    mhz = time_steps.clock_mhz
     flops = prefill_flops(nq, n_kv, x.q_pos0)
     tf = flops / (kms * 1e-3) / 1e12
     return {
@@ -404,6 +405,8 @@ def bench_e4m3(steps, warmup, n_kv=128000, seed=0):
                      "frac": round(tf / PEAK_E4M3_PREFILL_TFLOPS, 4),
                      "peak_note": "Q K^T at the fp8 peak, P V at the fp16 peak",
                      "frac_of_fp16_peak": round(tf / PEAK_F16_TFLOPS, 4),
+                     "clock_mhz": round(mhz, 1) if mhz else None,
+                     "frac_at_clock": round(tf / (PEAK_E4M3_PREFILL_TFLOPS * mhz / PEAK_CLOCK_MHZ), 4) if mhz else None,
                      "algorithmic_bytes": nq * 6 * 256 + 2 * n_kv * 256 + 2 * nq * 6 * 256,
                      "traffic": recorded_traffic().get(("prefill_causal_e4m3", e4m3_workload(n_kv)))},
     }

@@ -448,14 +448,14 @@ __device__ __forceinline__ void prefill_piece_e4m3(const PrefillParams& p, const
       asm volatile("" : "+v"(bk), "+v"(bv));
       f16x sc[1];
       sc[0] = f16x{};
-      v8i kf0 = read_k8_frag(kt, bk, kb, 0);
-      v8i kf1 = read_k8_frag(kt, bk, kb, 1);
-      sc[0] = mfma_fp8(kf0, qf[0], sc[0]);
-      kf0 = read_k8_frag(kt, bk, kb, 2);
-      sc[0] = mfma_fp8(kf1, qf[1], sc[0]);
-      kf1 = read_k8_frag(kt, bk, kb, 3);
-      sc[0] = mfma_fp8(kf0, qf[2], sc[0]);
-      sc[0] = mfma_fp8(kf1, qf[3], sc[0]);
+      // all four fragments in flight before the products
+      v8i kf[4];
+#pragma unroll
+      for (int si = 0; si < 4; ++si) kf[si] = read_k8_frag(kt, bk, kb, si);
+#pragma unroll
+      for (int si = 0; si < 4; ++si) sc[0] = mfma_fp8(kf[si], qf[si], sc[0]);
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0);
       h8 pk[1][2];
       softmax_32keys<1>(sc, acc, m, l, p.c, k0 + 31 > wpos_lo,
                         [&](int, int vv) { return k0 + lane_key(vv, half) <= pos; }, pk);
@@ -490,9 +490,23 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_e4m3(PrefillParams p) {
   __shared__ __attribute__((aligned(1024))) char k8a[kTileBytes8];
   __shared__ __attribute__((aligned(1024))) char k8b[kTileBytes8];
   const E4M3Lds sm = {{(GQA_LDS char*)v16a, (GQA_LDS char*)v16b}, {(GQA_LDS char*)k8a, (GQA_LDS char*)k8b}};
+  // profiling only, as in prefill_causal_fwd: shader cycles and wall ticks of the workgroup
+  const bool stamp = p.clk != nullptr && __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  unsigned long long c0 = 0, r0 = 0;
+  if (stamp) {
+    c0 = clock64();
+    r0 = wall_clock64();
+  }
   prefill_workgroup(p, [&](int b, int lo, int hi, bool full, int slot) {
     prefill_piece_e4m3<8>(p, sm, b, lo, hi, full, slot);
   });
+  if (stamp) {
+    const unsigned long long dc = clock64() - c0, dr = wall_clock64() - r0;
+    if (threadIdx.x == 0) {
+      atomicAdd(p.clk, dc);
+      atomicAdd(p.clk + 1, dr);
+    }
+  }
 }
 
 // Exact merge of the partials of q-blocks that were split across workgroups:
@@ -755,7 +769,7 @@ hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* 
   p.part_bytes = (uint32_t)prefill_workspace_bytes(s);
   p.c = scale * q_scale * k_scale * kLog2e;
   p.post = v_scale;
-  p.clk = nullptr;
+  p.clk = prof_clock();
   p.lse = nullptr;
   p.vdesc = nullptr;
   prof_before(stream);
