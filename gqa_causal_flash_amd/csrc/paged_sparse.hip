@@ -182,14 +182,31 @@ constexpr int kSubBytes = kSubKeys * kRowBytes;  // 16 KiB for K or V
 // j = 4(w%2) + i, which gives the lane offsets kl ^ 32j (K) and
 // vl ^ 128(j%4) (V) used by the dense kernel, shifted to the entry's
 // physical row.  Lanes 0..7 also record the logical position of row 8w+l.
-__device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk, rsrc_t rv, const int2* ent,
-                                                int e0, int e_end, char* kdst, char* vdst, int* kpos, int wave,
-                                                int lane, uint32_t kl, uint32_t vl) {
+// The wave's two entries (2w, 2w+1 of the sub-tile) are loaded a sub-tile
+// ahead by sub_entries(), so the gather addresses do not wait on them.
+struct SubEntries {
+  int2 e[2];
+};
+
+__device__ __forceinline__ SubEntries sub_entries(const int2* ent, int e0, int e_end, int wave) {
+  SubEntries s;
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const int e = e0 + 2 * wave + k;  // wave-uniform
+    const int2 x = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
+    // uniform values: kept in scalar registers
+    s.e[k] = int2{__builtin_amdgcn_readfirstlane(x.x), __builtin_amdgcn_readfirstlane(x.y)};
+  }
+  return s;
+}
+
+__device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk, rsrc_t rv, const SubEntries& se,
+                                                char* kdst, char* vdst, int* kpos, int wave, int lane, uint32_t kl,
+                                                uint32_t vl) {
   const int half = lane >> 5;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = e0 + 2 * wave + i / 2;  // wave-uniform
-    const int2 en = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
+    const int2 en = se.e[i / 2];
     const int u = 2 * (i & 1) + half;
     const bool live = en.x >= 0 && en.y + u < p.live_len;
     const uint32_t j = (uint32_t)(4 * (wave & 1) + i);
@@ -201,8 +218,7 @@ __device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk,
     load_lds_16B(rv, (GQA_LDS char*)(vdst + r0 * kRowBytes), vv, 0);
   }
   if (lane < 8) {
-    const int e = e0 + 2 * wave + lane / 4;
-    const int2 en = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
+    const int2 en = lane < 4 ? se.e[0] : se.e[1];
     const int u = lane & 3;
     const bool live = en.x >= 0 && en.y + u < p.live_len;
     kpos[8 * wave + lane] = live ? en.y + u : 0x7FFFFFFF;
@@ -266,17 +282,20 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   uint32_t bk = k_lane_base(lane);
   uint32_t bv = v_lane_base(lane);
 
-  auto issue = [&](int x) {
+  auto issue = [&](int x, const SubEntries& se) {
     const int buf = x & 1;
-    paged_issue_sub(p, rk, rv, ent, e_beg + 8 * x, e_end, smem + (2 + buf) * kSubBytes, smem + buf * kSubBytes,
-                    kpos_s[buf], wave, lane, kl, vl);
+    paged_issue_sub(p, rk, rv, se, smem + (2 + buf) * kSubBytes, smem + buf * kSubBytes, kpos_s[buf], wave, lane, kl,
+                    vl);
   };
-  if (s_lo < s_hi) issue(s_lo);
+  SubEntries nxt = sub_entries(ent, e_beg + 8 * s_lo, e_end, wave);
+  if (s_lo < s_hi) issue(s_lo, nxt);
+  nxt = sub_entries(ent, e_beg + 8 * (s_lo + 1), e_end, wave);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   for (int x = s_lo; x < s_hi; ++x) {
     const int buf = (x - s_lo) & 1;
-    if (x + 1 < s_hi) issue(x + 1);  // lands in the other slot
+    if (x + 1 < s_hi) issue(x + 1, nxt);  // lands in the other slot
+    nxt = sub_entries(ent, e_beg + 8 * (x + 2), e_end, wave);  // in flight during this sub-tile
     asm volatile("" : "+v"(bk), "+v"(bv));
     int kp[16];
 #pragma unroll
