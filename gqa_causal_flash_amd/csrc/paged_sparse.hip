@@ -60,6 +60,7 @@ struct PagedParams {
 // ------------------------------------------------------------------ prepass
 __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) {
   __shared__ unsigned long long keys[kSortMax];
+  __shared__ unsigned long long keys2[kSortMax];
   __shared__ int errs;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
@@ -113,26 +114,72 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     int npow = 1;
     while (npow < n) npow <<= 1;
     int bad = 0;
-    for (int i = tid; i < npow; i += kPrepassThreads) keys[i] = (i < n) ? translate(i, bad) : ~0ull;
+    // Bitonic sort, ascending, with the keys in registers: thread t holds
+    // elements t + 512 r (r < kSortMax / 512).  A compare-exchange at distance
+    // j pairs lanes of one wave when j < 64 (register shuffle, no barrier), a
+    // thread with itself when j >= 512, and otherwise goes through LDS (two
+    // buffers, one barrier per such stage).
+    constexpr int R = kSortMax / kPrepassThreads;
+    unsigned long long kv[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = tid + kPrepassThreads * r;
+      kv[r] = (i < n) ? translate(i, bad) : ~0ull;
+    }
     if (bad) atomicAdd(&errs, bad);
-    __syncthreads();
-    // bitonic sort, ascending
+    const int rmax = (npow + kPrepassThreads - 1) / kPrepassThreads;  // register slots in use
+    int buf = 0;
     for (int k = 2; k <= npow; k <<= 1) {
       for (int j = k >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < npow; i += kPrepassThreads) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const unsigned long long a = keys[i], c = keys[ixj];
-            const bool up = (i & k) == 0;
-            if ((a > c) == up) {
-              keys[i] = c;
-              keys[ixj] = a;
+        if (j >= kPrepassThreads) {
+          const int rj = j / kPrepassThreads;
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            const int rp = r ^ rj;
+            const int i = tid + kPrepassThreads * r;
+            if (rp > r && i < npow) {
+              const bool up = (i & k) == 0;
+              const unsigned long long a = kv[r], c = kv[rp];
+              if ((a > c) == up) {
+                kv[r] = c;
+                kv[rp] = a;
+              }
             }
           }
+        } else if (j < 64) {
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (r >= rmax) break;
+            const int i = tid + kPrepassThreads * r;
+            const unsigned long long a = kv[r];
+            const unsigned long long c = __shfl_xor(a, j);
+            const bool up = (i & k) == 0;
+            const bool lo = (i & j) == 0;  // the lower index of the pair keeps the smaller key when ascending
+            kv[r] = (lo == up) ? (a < c ? a : c) : (a < c ? c : a);
+          }
+        } else {
+          unsigned long long* kb = buf ? keys2 : keys;
+#pragma unroll
+          for (int r = 0; r < R; ++r)
+            if (r < rmax) kb[tid + kPrepassThreads * r] = kv[r];
+          __syncthreads();
+#pragma unroll
+          for (int r = 0; r < R; ++r) {
+            if (r >= rmax) break;
+            const int i = tid + kPrepassThreads * r;
+            const unsigned long long a = kv[r], c = kb[i ^ j];
+            const bool up = (i & k) == 0;
+            const bool lo = (i & j) == 0;
+            kv[r] = (lo == up) ? (a < c ? a : c) : (a < c ? c : a);
+          }
+          buf ^= 1;
         }
-        __syncthreads();
       }
     }
+#pragma unroll
+    for (int r = 0; r < R; ++r)
+      if (r < rmax) keys[tid + kPrepassThreads * r] = kv[r];
+    __syncthreads();
     // drop duplicates (same physical row) and count the valid prefix
     int dup = 0, valid = 0;
     for (int i = tid; i < n; i += kPrepassThreads) {
