@@ -86,3 +86,20 @@ def test_varlen_deterministic():
     a, la = _gpu(x)
     b, lb = _gpu(x)
     assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_varlen_benchmark_batch_sampled_rows():
+    """The benchmark's chunked-prefill batch (8 requests, seed 0) in the launch it times,
+    checked on 16 sampled query tokens of every request against the causal oracle of
+    that request's own slices (the definition the varlen pins fix)."""
+    kv, ql = workloads.varlen_batch_lengths(0)
+    x = workloads.varlen_inputs(kv, ql, 0)
+    o, lse = _gpu(x)
+    rng = np.random.default_rng(77)
+    for i, (nkv, nq) in enumerate(zip(kv, ql)):
+        q0, k0 = int(x.cu_q[i]), int(x.cu_kv[i])
+        rows = np.unique(np.concatenate([[0, nq - 1], rng.choice(nq, 14, replace=False)]))
+        ref, ref_lse = oracle.prefill_causal(x.q[q0:q0 + nq], x.k[k0:k0 + nkv], x.v[k0:k0 + nkv], int(nkv - nq),
+                                             x.scale, rows=rows)
+        assert_parity(o[q0 + rows], ref, f"request {i} (kv {nkv}, q {nq})")
+        assert np.abs(lse[q0 + rows].astype(np.float64) - ref_lse).max() <= TOL_LSE, f"request {i} lse"
