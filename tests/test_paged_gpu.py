@@ -45,6 +45,25 @@ def test_paged_128_entry_table():
     assert_parity(_gpu(x), _oracle(x), "128-entry table")
 
 
+def test_paged_hybrid_784_16_geometry():
+    """Hybrid geometry: the cache is stored in pages of 784 tokens and addressed by a
+    non-monotonic 128-entry page-16 table whose entries name 16-token sub-pages of
+    those pages (784 = 49 x 16).  A 784-token page is 49 contiguous 16-token pages,
+    so the page-16 path serves it over the same memory viewed as 49x as many pages."""
+    n784 = 3
+    x = workloads.paged_sparse_inputs(select_tokens=512, tail=3, seed=8, nq=2044, n_pages=49 * n784)
+    assert x.page_table.size == 128 and x.page_table.max() < 49 * n784
+    k784 = x.k_cache.reshape(n784, 784, 1, 256)  # the storage as 784-token pages
+    v784 = x.v_cache.reshape(n784, 784, 1, 256)
+    # the sub-page view addresses the same tokens as (page p // 49, offset 16 (p % 49) + j)
+    pg = x.page_table
+    toks = np.arange(x.live_len)
+    sub = pg[toks // 16]
+    assert np.array_equal(k784[sub // 49, 16 * (sub % 49) + toks % 16], x.k_cache[sub, toks % 16])
+    out = _gpu(x, k_cache=k784.reshape(-1, 16, 1, 256), v_cache=v784.reshape(-1, 16, 1, 256))
+    assert_parity(out, _oracle(x), "hybrid 784/16")
+
+
 def test_paged_stale_poison():
     """NaN in every cache slot holding no live token changes nothing and stays out of the output."""
     x = workloads.paged_sparse_inputs(select_tokens=512, tail=2, seed=11)
