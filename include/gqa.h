@@ -232,9 +232,10 @@ gqa_status gqa_verify_fp8kv(const void* q, const uint8_t* k_e4m3, const uint8_t*
  * HIP events plus one 16-byte device buffer, allocated by the first
  * gqa_profile_start() on a device and kept until the process ends.
  *
- * While profiling is on, the dense causal prefill kernel also adds the
- * lifetime of each of its workgroups in shader clock cycles (s_memtime) and
- * in constant-rate wall-clock ticks (s_memrealtime) to that buffer.
+ * While profiling is on, the dense causal prefill kernels (fp16 and E4M3)
+ * also add the lifetime of each of their workgroups in shader clock cycles
+ * (s_memtime) and in constant-rate wall-clock ticks (s_memrealtime) to that
+ * buffer.
  * gqa_profile_clock_mhz() then returns the average shader clock those
  * kernels ran at in the last stopped session, in MHz (0 if none ran or the
  * buffer could not be allocated): the clock against which the matrix-core
