@@ -110,6 +110,10 @@ def _workspace(nbytes: int, device, workspace):
         return None, 0
     if workspace is None:
         workspace = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    if not isinstance(workspace, torch.Tensor) or not workspace.is_cuda:
+        raise ValueError("workspace must be a tensor in device memory")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
     if workspace.numel() * workspace.element_size() < nbytes:
         raise ValueError("workspace too small")
     return workspace, workspace.numel() * workspace.element_size()

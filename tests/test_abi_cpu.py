@@ -212,3 +212,12 @@ def _e4m3(**kw):
 ])
 def test_e4m3_prefill_rejects_before_launch(kw, status):
     assert _e4m3(**kw) == status
+
+
+def test_binding_rejects_host_workspace():
+    """A workspace in host memory is refused before any call reaches the library."""
+    import torch
+
+    with pytest.raises(ValueError, match="device memory"):
+        g._workspace(1024, torch.device("cpu"), torch.empty(1024, dtype=torch.uint8))
+    assert g._workspace(0, torch.device("cpu"), None) == (None, 0)
