@@ -89,17 +89,24 @@ def _stream(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def _dev(t, dtype, name):
+def _dev(t, dtype, name, shape=None):
+    """Device pointer of a contiguous tensor of the given dtype (and shape, when given).
+
+    The kernels size every buffer from the call's arguments, not from the
+    allocation, so outputs and secondary inputs are checked against the shape
+    those arguments imply before their pointers reach the library."""
     import torch
 
     if not isinstance(t, torch.Tensor):
         raise TypeError(f"{name} must be a torch tensor")
-    if t.dtype != dtype:
+    if dtype is not None and t.dtype != dtype:
         raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
     if not t.is_cuda:
         raise ValueError(f"{name} must be in device memory")
     if not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
     return ctypes.c_void_p(t.data_ptr())
 
 
@@ -139,8 +146,9 @@ def gqa_prefill_causal(q, k, v, q_pos0: int, scale: float, o=None, workspace=Non
         o = torch.empty_like(q)
     nbytes = gqa_prefill_causal_workspace_size(nq, n_kv, q_pos0, hq, hkv, d)
     ws, ws_bytes = _workspace(nbytes, q.device, workspace)
-    st = lib().gqa_prefill_causal(_dev(q, torch.float16, "q"), _dev(k, torch.float16, "k"),
-                                  _dev(v, torch.float16, "v"), _dev(o, torch.float16, "o"), nq, n_kv, q_pos0, hq, hkv,
+    st = lib().gqa_prefill_causal(_dev(q, torch.float16, "q"), _dev(k, torch.float16, "k", (n_kv, hkv, d)),
+                                  _dev(v, torch.float16, "v"), _dev(o, torch.float16, "o", q.shape), nq, n_kv, q_pos0, hq,
+                                  hkv,
                                   d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
                                   _stream(stream))
     _check(st, "gqa_prefill_causal")
@@ -161,8 +169,9 @@ def gqa_prefill_causal_e4m3(q8, q_scale: float, k8, k_scale: float, v8, v_scale:
         o = torch.empty((nq, hq, d), dtype=torch.float16, device=q8.device)
     nbytes = gqa_prefill_causal_workspace_size(nq, n_kv, q_pos0, hq, hkv, d)
     ws, ws_bytes = _workspace(nbytes, q8.device, workspace)
-    st = lib().gqa_prefill_causal_e4m3(_dev(q8, torch.uint8, "q"), q_scale, _dev(k8, torch.uint8, "k"), k_scale,
-                                       _dev(v8, torch.uint8, "v"), v_scale, _dev(o, torch.float16, "o"), nq, n_kv,
+    st = lib().gqa_prefill_causal_e4m3(_dev(q8, torch.uint8, "q"), q_scale, _dev(k8, torch.uint8, "k", (n_kv, hkv, d)),
+                                       k_scale, _dev(v8, torch.uint8, "v"), v_scale,
+                                       _dev(o, torch.float16, "o", (nq, hq, d)), nq, n_kv,
                                        q_pos0, hq, hkv, d, scale,
                                        None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
                                        _stream(stream))
@@ -198,9 +207,10 @@ def gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, scale: float, o=None, lse=No
     nbytes = gqa_prefill_causal_varlen_workspace_size(batch, total_q, hq, hkv, d)
     ws, ws_bytes = _workspace(nbytes, q.device, workspace)
     st = lib().gqa_prefill_causal_varlen(
-        _dev(q, torch.float16, "q"), _dev(k, torch.float16, "k"), _dev(v, torch.float16, "v"),
-        _dev(o, torch.float16, "o"), None if lse is None else _dev(lse, torch.float32, "lse"),
-        _dev(cu_q, torch.int32, "cu_q"), _dev(cu_kv, torch.int32, "cu_kv"), batch, total_q, total_kv, hq, hkv, d,
+        _dev(q, torch.float16, "q"), _dev(k, torch.float16, "k", (total_kv, hkv, d)), _dev(v, torch.float16, "v"),
+        _dev(o, torch.float16, "o", q.shape), None if lse is None else _dev(lse, torch.float32, "lse", (total_q, hq)),
+        _dev(cu_q, torch.int32, "cu_q", (batch + 1,)), _dev(cu_kv, torch.int32, "cu_kv", (batch + 1,)), batch, total_q,
+        total_kv, hq, hkv, d,
         scale, ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream(stream))
     _check(st, "gqa_prefill_causal_varlen")
     return o, lse, ws
@@ -209,7 +219,7 @@ def gqa_prefill_causal_varlen(q, k, v, cu_q, cu_kv, scale: float, o=None, lse=No
 def gqa_prefill_causal_varlen_skipped(workspace, stream=None) -> int:
     """Sequences the last varlen call on `workspace` skipped as invalid (synchronises the stream)."""
     n = ctypes.c_int32(0)
-    _check(lib().gqa_prefill_causal_varlen_skipped(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(n),
+    _check(lib().gqa_prefill_causal_varlen_skipped(_dev(workspace, None, "workspace"), ctypes.byref(n),
                                                    _stream(stream)), "gqa_prefill_causal_varlen_skipped")
     return n.value
 
@@ -258,12 +268,14 @@ def gqa_prefill_paged_sparse(q, k_cache, v_cache, page_table, qblock_offsets, kv
         o = torch.empty_like(q)
     nbytes = gqa_prefill_paged_sparse_workspace_size(nq, n_ids, qblock_rows, kv_block_tokens, hq, hkv, d)
     ws, ws_bytes = _workspace(nbytes, q.device, workspace)
+    n_qblocks = -(-nq // qblock_rows) if qblock_rows > 0 else 0
     st = lib().gqa_prefill_paged_sparse(
-        _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache"), _dev(v_cache, torch.float16, "v_cache"),
-        _dev(page_table, torch.int32, "page_table"), page_table.numel(), n_pages, page_size,
-        _dev(qblock_offsets, torch.int32, "qblock_offsets"),
-        _dev(kv_block_ids, torch.int32, "kv_block_ids") if n_ids else None, n_ids, qblock_rows, kv_block_tokens, nq,
-        q_pos0, live_len, hq, hkv, d, scale, _dev(o, torch.float16, "o"),
+        _dev(q, torch.float16, "q"), _dev(k_cache, torch.float16, "k_cache", (n_pages, page_size, hkv, d)),
+        _dev(v_cache, torch.float16, "v_cache"),
+        _dev(page_table, torch.int32, "page_table", (page_table.numel(),)), page_table.numel(), n_pages, page_size,
+        _dev(qblock_offsets, torch.int32, "qblock_offsets", (n_qblocks + 1,)),
+        _dev(kv_block_ids, torch.int32, "kv_block_ids", (n_ids,)) if n_ids else None, n_ids, qblock_rows,
+        kv_block_tokens, nq, q_pos0, live_len, hq, hkv, d, scale, _dev(o, torch.float16, "o", q.shape),
         None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes, _stream(stream))
     _check(st, "gqa_prefill_paged_sparse")
     return o, ws
@@ -272,7 +284,7 @@ def gqa_prefill_paged_sparse(q, k_cache, v_cache, page_table, qblock_offsets, kv
 def gqa_prefill_paged_sparse_dropped(workspace, stream=None) -> int:
     """Index entries the last paged call on `workspace` dropped as invalid (synchronises the stream)."""
     n = ctypes.c_int32(0)
-    _check(lib().gqa_prefill_paged_sparse_dropped(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(n),
+    _check(lib().gqa_prefill_paged_sparse_dropped(_dev(workspace, None, "workspace"), ctypes.byref(n),
                                                   _stream(stream)), "gqa_prefill_paged_sparse_dropped")
     return n.value
 
@@ -298,8 +310,9 @@ def gqa_verify_fp8kv(q, k_e4m3, v_e4m3, k_scale: float, v_scale: float, scale: f
         o = torch.empty_like(q)
     nbytes = gqa_verify_fp8kv_workspace_size(nq, n_kv, hq, hkv, d)
     ws, ws_bytes = _workspace(nbytes, q.device, workspace)
-    st = lib().gqa_verify_fp8kv(_dev(q, torch.float16, "q"), _dev(k_e4m3, torch.uint8, "k_e4m3"),
-                                _dev(v_e4m3, torch.uint8, "v_e4m3"), k_scale, v_scale, _dev(o, torch.float16, "o"), nq,
+    st = lib().gqa_verify_fp8kv(_dev(q, torch.float16, "q"), _dev(k_e4m3, torch.uint8, "k_e4m3", (n_kv, hkv, d)),
+                                _dev(v_e4m3, torch.uint8, "v_e4m3"), k_scale, v_scale,
+                                _dev(o, torch.float16, "o", q.shape), nq,
                                 n_kv, hq, hkv, d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()),
                                 ws_bytes, _stream(stream))
     _check(st, "gqa_verify_fp8kv")

@@ -221,3 +221,17 @@ def test_binding_rejects_host_workspace():
     with pytest.raises(ValueError, match="device memory"):
         g._workspace(1024, torch.device("cpu"), torch.empty(1024, dtype=torch.uint8))
     assert g._workspace(0, torch.device("cpu"), None) == (None, 0)
+
+
+def test_binding_checks_shapes_before_pointers_leave():
+    """The kernels size buffers from the call's arguments: a mismatched output or cache shape is refused."""
+    import torch
+
+    t = torch.empty((4, 6, 256), dtype=torch.float16)
+    with pytest.raises(ValueError, match="device memory"):  # checked in order: placement first
+        g._dev(t, torch.float16, "o", (4, 6, 256))
+    if not torch.cuda.is_available():
+        return
+    d = t.cuda()
+    with pytest.raises(ValueError, match="shape"):
+        g._dev(d, torch.float16, "o", (5, 6, 256))
