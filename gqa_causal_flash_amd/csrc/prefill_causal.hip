@@ -512,40 +512,70 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_e4m3(PrefillParams p) {
 // Exact merge of the partials of q-blocks that were split across workgroups:
 // M = max_k m_k, O = sum_k 2^(m_k - M) acc_k / sum_k 2^(m_k - M) l_k, and
 // lse = (M + log2 sum_k 2^(m_k - M) l_k) ln 2.  Thread (row rl of the slots,
-// 64 columns from 64*dq) combines slots slot_lo .. slot_hi into output row
-// `orow` of p.o (and p.lse).
+// columns 32 dq .. 32 dq + 31) combines slots slot_lo .. slot_hi into output
+// row `orow` of p.o (and p.lse).  Slots are taken in groups of four, then
+// two, then one, with every load of a group issued before any of it is summed.
+constexpr int kMergeCols = 32;                              // columns per merge thread
+constexpr int kMergeThreadsPerRow = kHeadDim / kMergeCols;  // 8
+constexpr int kMergeRowsPerWG = 256 / kMergeThreadsPerRow;  // 32
+
+template <int G>
+__device__ __forceinline__ void merge_group(rsrc_t rp, int w0, int rl, int dq, float M, f4 (&o)[8], float& L) {
+  const uint32_t slot_bytes = (uint32_t)(kPartialFloats * 4);
+  float mw[G], lw[G];
+  u4 x[G][8];
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const uint32_t sb = (uint32_t)(w0 + i) * slot_bytes;
+    mw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
+    lw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((8 * dq + j) * kRowsPerBlock + rl) * 16), 0, 0);
+  }
+  __builtin_amdgcn_sched_barrier(0);  // keep every load of the group ahead of the sums
+#pragma unroll
+  for (int i = 0; i < G; ++i) {
+    const float aw = (mw[i] == -INFINITY) ? 0.f : fast_exp2(mw[i] - M);
+    L += aw * lw[i];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) o[j] += aw * __builtin_bit_cast(f4, x[i][j]);
+  }
+}
+
 __device__ __forceinline__ void merge_row(const PrefillParams& p, int slot_lo, int slot_hi, int rl, int dq, int orow) {
   const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
+  const uint32_t slot_bytes = (uint32_t)(kPartialFloats * 4);
   float M = -INFINITY;
-  for (int w = slot_lo; w <= slot_hi; ++w) {
-    const uint32_t sb = (uint32_t)w * (uint32_t)(kPartialFloats * 4);
-    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0)));
-  }
-  f4 o[16];
+  for (int w0 = slot_lo; w0 <= slot_hi; w0 += 8) {
+    float mv[8];
 #pragma unroll
-  for (int j = 0; j < 16; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
+    for (int i = 0; i < 8; ++i)
+      mv[i] = __uint_as_float(
+          __builtin_amdgcn_raw_buffer_load_b32(rp, min(w0 + i, slot_hi) * slot_bytes + (kPartM + rl) * 4, 0, 0));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) M = fmaxf(M, mv[i]);
+  }
+  f4 o[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int w = slot_lo; w <= slot_hi; ++w) {
-    const uint32_t sb = (uint32_t)w * (uint32_t)(kPartialFloats * 4);
-    const float mw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
-    const float lw = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
-    const float aw = (mw == -INFINITY) ? 0.f : fast_exp2(mw - M);
-    L += aw * lw;
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const u4 x = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((16 * dq + j) * kRowsPerBlock + rl) * 16), 0, 0);
-      o[j] += aw * __builtin_bit_cast(f4, x);
-    }
+  int w0 = slot_lo;
+  for (; w0 + 3 <= slot_hi; w0 += 4) merge_group<4>(rp, w0, rl, dq, M, o, L);
+  if (w0 + 1 <= slot_hi) {
+    merge_group<2>(rp, w0, rl, dq, M, o, L);
+    w0 += 2;
   }
+  if (w0 <= slot_hi) merge_group<1>(rp, w0, rl, dq, M, o, L);
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-  const uint32_t obase = (uint32_t)orow * kRowBytes + 128 * dq;
+  const uint32_t obase = (uint32_t)orow * kRowBytes + 2 * kMergeCols * dq;
 #pragma unroll
-  for (int j = 0; j < 16; j += 2) {
+  for (int j = 0; j < 8; j += 2) {
     const h2 a0 = cvt2(o[j][0] * inv, o[j][1] * inv), a1 = cvt2(o[j][2] * inv, o[j][3] * inv);
     const h2 b0 = cvt2(o[j + 1][0] * inv, o[j + 1][1] * inv), b1 = cvt2(o[j + 1][2] * inv, o[j + 1][3] * inv);
-    const h8 x = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
-    store_16B(ro, obase + j * 8, __builtin_bit_cast(u4, x));
+    const h8 xx = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
+    store_16B(ro, obase + j * 8, __builtin_bit_cast(u4, xx));
   }
   if (p.lse != nullptr && dq == 0) {
     const rsrc_t rl_ = make_rsrc(p.lse, (uint32_t)p.nrows * 4);
@@ -553,11 +583,11 @@ __device__ __forceinline__ void merge_row(const PrefillParams& p, int slot_lo, i
   }
 }
 
-// Workgroup (b, quarter): 64 rows of q-block b; thread (row, 64 columns).
+// Workgroup (b, part): 32 rows of q-block b; thread (row, 32 columns).
 __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
-  constexpr int kParts = kRowsPerBlock / 64;
+  constexpr int kParts = kRowsPerBlock / kMergeRowsPerWG;
   const int b = blockIdx.x / kParts;
-  const int quarter = blockIdx.x % kParts;
+  const int part = blockIdx.x % kParts;
   int w0, w1, slot0;
   if (p.split > 0) {  // pieces of q-block b are slots b*split .. b*split + split - 1
     w0 = 0;
@@ -573,8 +603,8 @@ __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   }
   if (w0 == w1) return;  // done whole by one workgroup, already written
   const int tid = threadIdx.x;
-  const int rl = quarter * 64 + (tid & 63);
-  merge_row(p, w0 + slot0, w1 + slot0, rl, tid >> 6, b * kRowsPerBlock + rl);
+  const int rl = part * kMergeRowsPerWG + tid % kMergeRowsPerWG;
+  merge_row(p, w0 + slot0, w1 + slot0, rl, tid / kMergeRowsPerWG, b * kRowsPerBlock + rl);
 }
 
 // ------------------------------------------------------------------ varlen
@@ -698,17 +728,17 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_varlen(PrefillParams p)
 }
 
 __global__ __launch_bounds__(256) void prefill_merge_varlen(PrefillParams p) {
-  constexpr int kParts = kRowsPerBlock / 64;
+  constexpr int kParts = kRowsPerBlock / kMergeRowsPerWG;
   const int qb = blockIdx.x / kParts;
-  const int quarter = blockIdx.x % kParts;
+  const int part = blockIdx.x % kParts;
   PrefillParams s;
   int jblk;
   if (!varlen_block(p, qb, s, jblk)) return;
   const int tid = threadIdx.x;
-  const int rl = quarter * 64 + (tid & 63);
+  const int rl = part * kMergeRowsPerWG + tid % kMergeRowsPerWG;
   const int orow = jblk * kRowsPerBlock + rl;
   if (orow >= s.nrows) return;
-  merge_row(s, qb * p.split, qb * p.split + p.split - 1, rl, tid >> 6, orow);
+  merge_row(s, qb * p.split, qb * p.split + p.split - 1, rl, tid / kMergeRowsPerWG, orow);
 }
 
 }  // namespace
@@ -742,7 +772,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   prof_after(stream);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
-    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
@@ -778,7 +808,7 @@ hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* 
   prof_after(stream);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
-    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / 64)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
@@ -825,7 +855,7 @@ hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void
   e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess || vs.split == 1) return e;
-  hipLaunchKernelGGL(prefill_merge_varlen, dim3(vs.cap * (kRowsPerBlock / 64)), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(prefill_merge_varlen, dim3(vs.cap * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 
