@@ -17,8 +17,8 @@
 // (q = 6..8) wave c holds rows 32c .. 32c+31 and both compute every tile,
 // kRing - 1 tiles ahead of the loads; with at most 32 (q = 1..5, the
 // single-row tail included) both waves hold all the rows and take alternate
-// tiles, two tiles ahead, and combine their states before the workgroup
-// writes its partial.  The bytes are decoded to fp16 in registers, right
+// tiles with three tiles in flight, and combine their states before the
+// workgroup writes its partial.  The bytes are decoded to fp16 in registers, right
 // where the matrix cores take them:
 //   K fragments (S^T = K Q^T, A operand) by an 8-byte LDS read per lane;
 //     the head-dimension order of the product is permuted so that lane half h
@@ -186,27 +186,41 @@ __global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
   };
 
   if constexpr (PAIR) {
-    // double step d takes tiles 2d (wave 0) and 2d + 1 (wave 1) from slot pair
-    // d % 2; the tiles of double step d + 1 load into the other pair meanwhile
-    if (0 < n) issue(ring.s[0], t_lo);
-    if (1 < n) issue(ring.s[1], t_lo + 1);
-    // the loop is written once per wave so that every slot a wave reads is a
-    // compile-time choice (the compiler then knows the reads miss the slots
-    // being loaded)
+    // tile j of the range sits in ring slot j % kRing; step s computes tiles
+    // 2s (wave 0) and 2s + 1 (wave 1).  Three tiles are issued up front; step
+    // s waits for tiles 2s and 2s + 1 with tile 2s + 2 still in flight, then
+    // issues tiles 2s + 3 and 2s + 4 into the slots of tiles 2s - 2 and
+    // 2s - 1, which both waves finished in step s - 1.
+    static_assert(kRing == 5, "the pair pipeline keeps five tiles: two in use, three in flight");
+#pragma unroll
+    for (int j = 0; j < 3; ++j)
+      if (j < n) issue(ring.s[j], t_lo + j);
+    // the loop is written once per wave and unrolled over the ring, so that
+    // every slot a wave reads is a compile-time choice (the compiler then
+    // knows the reads miss the slots being loaded)
     auto run = [&](auto wavec) {
       constexpr int WV = decltype(wavec)::value;
-      auto dstep = [&](auto pairc, int d) {
-        constexpr int P = decltype(pairc)::value;
-        asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();  // tiles 2d, 2d + 1 are in; the other pair's tiles have been used
-        if (2 * d + 2 < n) issue(ring.s[2 * (P ^ 1)], t_lo + 2 * d + 2);
-        if (2 * d + 3 < n) issue(ring.s[2 * (P ^ 1) + 1], t_lo + 2 * d + 3);
-        if (2 * d + WV < n) compute((const GQA_LDS char*)ring.s[2 * P + WV], t_lo + 2 * d + WV);
+      auto step = [&](auto sc, int st) {
+        constexpr int S = decltype(sc)::value;  // st % kRing
+        if (2 * st + 2 < n)
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 2s + 2 may stay in flight
+        else
+          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+        lds_barrier();
+        if (2 * st + 3 < n) issue(ring.s[(2 * S + 3) % kRing], t_lo + 2 * st + 3);
+        if (2 * st + 4 < n) issue(ring.s[(2 * S + 4) % kRing], t_lo + 2 * st + 4);
+        if (2 * st + WV < n) compute((const GQA_LDS char*)ring.s[(2 * S + WV) % kRing], t_lo + 2 * st + WV);
       };
-      for (int d = 0; 2 * d < n; d += 2) {
-        dstep(std::integral_constant<int, 0>{}, d);
-        if (2 * d + 2 >= n) break;
-        dstep(std::integral_constant<int, 1>{}, d + 1);
+      for (int st = 0; 2 * st < n; st += kRing) {
+        step(std::integral_constant<int, 0>{}, st);
+        if (2 * st + 2 >= n) break;
+        step(std::integral_constant<int, 1>{}, st + 1);
+        if (2 * st + 4 >= n) break;
+        step(std::integral_constant<int, 2>{}, st + 2);
+        if (2 * st + 6 >= n) break;
+        step(std::integral_constant<int, 3>{}, st + 3);
+        if (2 * st + 8 >= n) break;
+        step(std::integral_constant<int, 4>{}, st + 4);
       }
     };
     if (wave == 0)
