@@ -11,15 +11,14 @@
 // into the softmax scale and the V scale into the final normalisation.
 //
 // The work is bound by HBM bandwidth (K + V = 512 B per key), so the key range
-// is split evenly over two workgroups per compute unit.  A workgroup of two
-// waves streams its keys in 32-key tiles of raw bytes through a ring of LDS
-// slots with direct HBM -> LDS loads.  With more than 32 packed query rows
-// (q = 6..8) wave c holds rows 32c .. 32c+31 and both compute every tile,
-// kRing - 1 tiles ahead of the loads; with at most 32 (q = 1..5, the
-// single-row tail included) both waves hold all the rows and take alternate
-// tiles with three tiles in flight, and combine their states before the
-// workgroup writes its partial.  The bytes are decoded to fp16 in registers, right
-// where the matrix cores take them:
+// is split evenly over two workgroups per compute unit.  A workgroup streams
+// its keys in 32-key tiles of raw bytes through a ring of five LDS slots with
+// direct HBM -> LDS loads, three tiles in flight.  It has two waves per
+// 32-row block of packed query rows (one block for q = 1..5, the single-row
+// tail included; two for q = 6..8): the two waves of a block take alternate
+// tiles and combine their states before the workgroup writes its partial.
+// The bytes are decoded to fp16 in registers, right where the matrix cores
+// take them:
 //   K fragments (S^T = K Q^T, A operand) by an 8-byte LDS read per lane;
 //     the head-dimension order of the product is permuted so that lane half h
 //     covers columns 128h .. 128h+127 (Q is loaded in the same order);
@@ -85,11 +84,18 @@ struct RawRing {
   char* s[kRing];
 };
 
-// PAIR (at most 32 packed rows): both waves hold all the rows and compute
-// alternate tiles, each leaving its own partial; otherwise wave c holds rows
-// 32c .. 32c+31 and both compute every tile.
-template <bool PAIR>
-__global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
+// RB row blocks of 32 packed rows (RB = 1 for at most 32 rows, 2 for up to
+// 64).  Wave w holds row block w % RB and takes the tiles of parity w / RB:
+// the two waves of a row block compute alternate tiles, each keeping its own
+// online-softmax state, and combine before the workgroup writes its partial.
+// Every wave stages 16 / (2 RB) of the 16 KiB-pieces of each tile (K pieces
+// first, then V).  At two workgroups per compute unit, RB = 2 puts two waves
+// on every SIMD, so one wave's decode and softmax overlap the other's matrix
+// products.
+template <int RB>
+__global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
+  constexpr int kWaves = 2 * RB;
+  constexpr int kLoads = 16 / kWaves;  // 1 KiB loads per tile and wave
   __shared__ __attribute__((aligned(1024))) char r0[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char r1[kSlotBytes];
   __shared__ __attribute__((aligned(1024))) char r2[kSlotBytes];
@@ -99,37 +105,41 @@ __global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
   const RawRing ring = {{r0, r1, r2, r3, r4}};
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // row block; also K (0) / V (1) loader
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int rb = wave % RB;  // row block
+  const int par = wave / RB;  // tile parity
   const int half = lane >> 5;
   const int col = lane & 31;
-  (void)tid;
 
   const int t_lo = (int)((long long)blockIdx.x * p.ntiles / p.grid);
   const int t_hi = (int)((long long)(blockIdx.x + 1) * p.ntiles / p.grid);
   const int n = t_hi - t_lo;  // >= 1
 
-  // this wave's loads: raw tile rows 4i .. 4i+3 per instruction, lane l taking
-  // row 4i + l/16 and physical chunk l % 16 (logical chunk (l % 16) ^ swz)
-  const rsrc_t rkv = make_rsrc(wave == 0 ? (const void*)p.k : (const void*)p.v, (uint32_t)p.n_kv * kFp8Row);
-  uint32_t loff[8];
+  // this wave's loads: 1 KiB pieces i = i0 .. i0 + kLoads - 1 of K (i < 8) or
+  // V (i >= 8), piece i holding raw rows 4(i%8) .. 4(i%8)+3; lane l takes row
+  // 4(i%8) + l/16 and physical chunk l % 16 (logical chunk (l % 16) ^ swz)
+  const int i0 = wave * kLoads;
+  const bool stage_v = i0 >= 8;
+  const rsrc_t rkv = make_rsrc(stage_v ? (const void*)p.v : (const void*)p.k, (uint32_t)p.n_kv * kFp8Row);
+  uint32_t loff[kLoads];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int r = 4 * i + (lane >> 4);
-    const uint32_t swz = wave == 0 ? k_swz(r) : v_swz(r);
-    loff[i] = (uint32_t)r * kFp8Row + 16u * ((uint32_t)(lane & 15) ^ swz);
+  for (int j = 0; j < kLoads; ++j) {
+    const int r = 4 * ((i0 + j) & 7) + (lane >> 4);
+    const uint32_t swz = stage_v ? v_swz(r) : k_swz(r);
+    loff[j] = (uint32_t)r * kFp8Row + 16u * ((uint32_t)(lane & 15) ^ swz);
   }
-  auto issue = [&](char* slot, int t) {  // raw bytes of tile t into a slot
-    GQA_LDS char* dst = (GQA_LDS char*)slot + wave * kRawTile;
+  const uint32_t ldst = (stage_v ? kRawTile : 0) + 1024u * (uint32_t)(i0 & 7);
+  auto issue = [&](char* slot, int t) {  // this wave's pieces of tile t into a slot
+    GQA_LDS char* dst = (GQA_LDS char*)slot + ldst;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) load_lds_16B(rkv, dst + i * 1024, loff[i], (uint32_t)t * kRawTile);
+    for (int j = 0; j < kLoads; ++j) load_lds_16B(rkv, dst + j * 1024, loff[j], (uint32_t)t * kRawTile);
   };
 
-  const int row = (PAIR ? 0 : 32 * wave) + col;
-  const bool rows_active = PAIR || 32 * wave < p.nrows;
+  const int row = 32 * rb + col;
   const int pos = (p.n_kv - p.nq) + min(row, p.nrows - 1) / kGroup;
   const int pos_min = p.n_kv - p.nq;  // first query position
   // Q as B fragments in the permuted column order: step s, lane half h holds
-  // columns 128h + 8s .. 128h + 8s + 7
+  // columns 128h + 8s .. 128h + 8s + 7 (rows past the last read as zeros)
   h8 qf[1][16];
   {
     const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
@@ -185,118 +195,94 @@ __global__ __launch_bounds__(128, 2) void verify_fwd(VerifyParams p) {
     }
   };
 
-  if constexpr (PAIR) {
-    // tile j of the range sits in ring slot j % kRing; step s computes tiles
-    // 2s (wave 0) and 2s + 1 (wave 1).  Three tiles are issued up front; step
-    // s waits for tiles 2s and 2s + 1 with tile 2s + 2 still in flight, then
-    // issues tiles 2s + 3 and 2s + 4 into the slots of tiles 2s - 2 and
-    // 2s - 1, which both waves finished in step s - 1.
-    static_assert(kRing == 5, "the pair pipeline keeps five tiles: two in use, three in flight");
+  // Tile j of the range sits in ring slot j % kRing; step s computes tiles 2s
+  // (parity 0) and 2s + 1 (parity 1).  Three tiles are issued up front; step
+  // s waits for tiles 2s and 2s + 1 with tile 2s + 2 still in flight, then
+  // issues tiles 2s + 3 and 2s + 4 into the slots of tiles 2s - 2 and 2s - 1,
+  // which every wave finished in step s - 1.
 #pragma unroll
-    for (int j = 0; j < 3; ++j)
-      if (j < n) issue(ring.s[j], t_lo + j);
-    // the loop is written once per wave and unrolled over the ring, so that
-    // every slot a wave reads is a compile-time choice (the compiler then
-    // knows the reads miss the slots being loaded)
-    auto run = [&](auto wavec) {
-      constexpr int WV = decltype(wavec)::value;
-      auto step = [&](auto sc, int st) {
-        constexpr int S = decltype(sc)::value;  // st % kRing
-        if (2 * st + 2 < n)
-          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");  // tile 2s + 2 may stay in flight
+  for (int j = 0; j < 3; ++j)
+    if (j < n) issue(ring.s[j], t_lo + j);
+  // the loop is written once per parity and unrolled over the ring, so that
+  // every slot a wave reads is a compile-time choice (the compiler then knows
+  // the reads miss the slots being loaded)
+  auto run = [&](auto parc) {
+    constexpr int PAR = decltype(parc)::value;
+    auto step = [&](auto sc, int st) {
+      constexpr int S = decltype(sc)::value;  // st % kRing
+      if (2 * st + 2 < n) {  // tile 2s + 2 may stay in flight
+        if constexpr (kLoads == 8)
+          asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
         else
-          asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-        lds_barrier();
-        if (2 * st + 3 < n) issue(ring.s[(2 * S + 3) % kRing], t_lo + 2 * st + 3);
-        if (2 * st + 4 < n) issue(ring.s[(2 * S + 4) % kRing], t_lo + 2 * st + 4);
-        if (2 * st + WV < n) compute((const GQA_LDS char*)ring.s[(2 * S + WV) % kRing], t_lo + 2 * st + WV);
-      };
-      for (int st = 0; 2 * st < n; st += kRing) {
-        step(std::integral_constant<int, 0>{}, st);
-        if (2 * st + 2 >= n) break;
-        step(std::integral_constant<int, 1>{}, st + 1);
-        if (2 * st + 4 >= n) break;
-        step(std::integral_constant<int, 2>{}, st + 2);
-        if (2 * st + 6 >= n) break;
-        step(std::integral_constant<int, 3>{}, st + 3);
-        if (2 * st + 8 >= n) break;
-        step(std::integral_constant<int, 4>{}, st + 4);
-      }
-    };
-    if (wave == 0)
-      run(std::integral_constant<int, 0>{});
-    else
-      run(std::integral_constant<int, 1>{});
-  } else {
-    // prologue: kRing - 1 tiles in flight, tile j in slot j
-#pragma unroll
-    for (int j = 0; j < kRing - 1; ++j)
-      if (j < n) issue(ring.s[j], t_lo + j);
-
-    // iteration it computes tile t_lo + it from slot it % kRing
-    auto step = [&](auto slotc, int it) {
-      constexpr int SL = decltype(slotc)::value;
-      const int t = t_lo + it;
-      // tile t has landed once at most min(n - 1 - it, kRing - 2) later tiles are outstanding
-      const int later = min(n - 1 - it, kRing - 2);
-      if (later >= 3)
-        asm volatile("s_waitcnt vmcnt(24)" ::: "memory");
-      else if (later == 2)
-        asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
-      else if (later == 1)
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      else
+          asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
+      } else {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      lds_barrier();  // both halves of tile t are in; the slot of tile t-1 is free
-      if (it + kRing - 1 < n) issue(ring.s[(SL + kRing - 1) % kRing], t + kRing - 1);
-      if (rows_active) compute((const GQA_LDS char*)ring.s[SL], t);
+      }
+      lds_barrier();
+      if (2 * st + 3 < n) issue(ring.s[(2 * S + 3) % kRing], t_lo + 2 * st + 3);
+      if (2 * st + 4 < n) issue(ring.s[(2 * S + 4) % kRing], t_lo + 2 * st + 4);
+      if (2 * st + PAR < n) compute((const GQA_LDS char*)ring.s[(2 * S + PAR) % kRing], t_lo + 2 * st + PAR);
     };
-    for (int it = 0; it < n; it += kRing) {
-      step(std::integral_constant<int, 0>{}, it);
-      if (it + 1 >= n) break;
-      step(std::integral_constant<int, 1>{}, it + 1);
-      if (it + 2 >= n) break;
-      step(std::integral_constant<int, 2>{}, it + 2);
-      if (it + 3 >= n) break;
-      step(std::integral_constant<int, 3>{}, it + 3);
-      if (it + 4 >= n) break;
-      step(std::integral_constant<int, 4>{}, it + 4);
+    for (int st = 0; 2 * st < n; st += kRing) {
+      step(std::integral_constant<int, 0>{}, st);
+      if (2 * st + 2 >= n) break;
+      step(std::integral_constant<int, 1>{}, st + 1);
+      if (2 * st + 4 >= n) break;
+      step(std::integral_constant<int, 2>{}, st + 2);
+      if (2 * st + 6 >= n) break;
+      step(std::integral_constant<int, 3>{}, st + 3);
+      if (2 * st + 8 >= n) break;
+      step(std::integral_constant<int, 4>{}, st + 4);
     }
-  }
+  };
+  if (par == 0)
+    run(std::integral_constant<int, 0>{});
+  else
+    run(std::integral_constant<int, 1>{});
 
+  // The parity-1 wave of each row block hands its state to the parity-0 wave
+  // through LDS (the ring is idle now): both hold the same rows in the same
+  // lanes, so the parity-0 wave combines register by register,
+  // O = 2^(m1-M) O1 + 2^(m2-M) O2 and likewise l.  Accumulator j of row block
+  // b sits in ring slot 2b + j / 64 at float (j % 64) * 64 + lane; m and l in
+  // slot 4 at float (2b + {0, 1}) * 64 + lane.
   float lt = swap_halves_sum(l[0]);
-  if constexpr (PAIR) {
-    // wave 1 hands its state to wave 0 through LDS (the ring is idle now): the
-    // two waves hold the same rows in the same lanes, so wave 0 combines
-    // register by register, O = 2^(m1-M) O1 + 2^(m2-M) O2 and likewise l.
-    // Value j of a lane (128 accumulators, m, l) sits in ring slot j / 64 at
-    // float (j % 64) * 64 + lane.
-    auto xv = [&](int j) -> GQA_LDS float& {
-      return ((GQA_LDS float*)ring.s[j >> 6])[(j & 63) * 64 + lane];
-    };
-    lds_barrier();  // every wave is done with the ring
-    if (wave == 1) {
+  lds_barrier();  // every wave is done with the ring
+  auto hand = [&](auto rbc, bool write) {
+    constexpr int B = decltype(rbc)::value;
+    auto xa = [&](int j) -> GQA_LDS float& { return ((GQA_LDS float*)ring.s[2 * B + (j >> 6)])[(j & 63) * 64 + lane]; };
+    GQA_LDS float* xm = (GQA_LDS float*)ring.s[4] + 2 * B * 64 + lane;
+    if (write) {
 #pragma unroll
       for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) xv(16 * dt + v) = acc[0][dt][v];
-      xv(128) = m[0];
-      xv(129) = lt;
+        for (int v = 0; v < 16; ++v) xa(16 * dt + v) = acc[0][dt][v];
+      xm[0] = m[0];
+      xm[64] = lt;
+      return;
     }
-    lds_barrier();
-    if (wave == 1) return;
-    const float m2 = xv(128), l2 = xv(129);
+    const float m2 = xm[0], l2 = xm[64];
     const float mm = fmaxf(m[0], m2);
     const float a1 = (m[0] == -INFINITY) ? 0.f : fast_exp2(m[0] - mm);
     const float a2 = (m2 == -INFINITY) ? 0.f : fast_exp2(m2 - mm);
 #pragma unroll
     for (int dt = 0; dt < 8; ++dt)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) acc[0][dt][v] = a1 * acc[0][dt][v] + a2 * xv(16 * dt + v);
+      for (int v = 0; v < 16; ++v) acc[0][dt][v] = a1 * acc[0][dt][v] + a2 * xa(16 * dt + v);
     m[0] = mm;
     lt = a1 * lt + a2 * l2;
-  }
-  if (rows_active && row < p.nrows) {
+  };
+  auto hand_rb = [&](bool write) {
+    if (RB == 1 || rb == 0)
+      hand(std::integral_constant<int, 0>{}, write);
+    else
+      hand(std::integral_constant<int, 1>{}, write);
+  };
+  if (par == 1) hand_rb(true);
+  lds_barrier();
+  if (par == 1) return;
+  hand_rb(false);
+  if (row < p.nrows) {
     // partial slot, row-major: acc[64 rows][256 columns], then m[64], l[64];
     // register 4g .. 4g+3 of tile dt holds columns 32dt + 8g + 4h .. +3
     const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
@@ -403,10 +389,10 @@ hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v
   p.c = scale * k_scale * kLog2e;
   p.v_scale = v_scale;
   prof_before(stream);
-  if (s.pair)
-    hipLaunchKernelGGL(verify_fwd<true>, dim3(s.grid), dim3(128), 0, stream, p);
+  if (s.row_blocks == 1)
+    hipLaunchKernelGGL(verify_fwd<1>, dim3(s.grid), dim3(128), 0, stream, p);
   else
-    hipLaunchKernelGGL(verify_fwd<false>, dim3(s.grid), dim3(128), 0, stream, p);
+    hipLaunchKernelGGL(verify_fwd<2>, dim3(s.grid), dim3(256), 0, stream, p);
   hipError_t e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess) return e;

@@ -20,13 +20,12 @@ constexpr int kVerifyMinTiles = 8;
 struct VerifySched {
   int ntiles;
   int grid;
-  bool pair;  // the two waves of a workgroup split the tiles (and combine before writing)
+  int row_blocks;  // 32-row blocks of packed rows: 1 (q <= 5) or 2 (q = 6..8)
 };
 
-// With at most 32 packed rows (q <= 5) one 32-row block holds them all, so the
-// workgroup's two waves both hold every row and take alternate tiles instead
-// of one row block each; they combine their states in LDS before the
-// workgroup writes its one partial.
+// Each workgroup has two waves per 32-row block; the two waves of a block
+// take alternate tiles and combine their states in LDS before the workgroup
+// writes its one partial.
 inline VerifySched verify_schedule(int nq, int n_kv, int hq) {
   VerifySched s;
   s.ntiles = (n_kv + 31) / 32;
@@ -34,7 +33,7 @@ inline VerifySched verify_schedule(int nq, int n_kv, int hq) {
   if (g < 1) g = 1;
   if (g > kVerifyMaxGrid) g = kVerifyMaxGrid;
   s.grid = g;
-  s.pair = nq * hq <= 32;
+  s.row_blocks = nq * hq <= 32 ? 1 : 2;
   return s;
 }
 
