@@ -29,8 +29,10 @@ def test_verify_parity_full_context(nq):
     assert_parity(_gpu(x), _oracle(x), f"q={nq} ctx=261888")
 
 
-@pytest.mark.parametrize("nq,ctx", [(1, 1), (1, 33), (5, 100), (8, 8), (8, 1000), (3, 4097), (6, 262144)])
+@pytest.mark.parametrize("nq,ctx", [(1, 1), (1, 33), (5, 100), (6, 100), (8, 8), (8, 1000), (3, 4097), (7, 4097),
+                                    (6, 262144)])
 def test_verify_parity_edges(nq, ctx):
+    """One 32-row block (q <= 5) and two (q = 6..8), with 1 to 16 tiles per workgroup, odd counts included."""
     x = workloads.verify_inputs(nq, ctx, seed=nq * 7 + ctx)
     assert_parity(_gpu(x), _oracle(x), f"q={nq} ctx={ctx}")
 
