@@ -147,9 +147,8 @@ def gqa_prefill_causal(q, k, v, q_pos0: int, scale: float, o=None, workspace=Non
     nbytes = gqa_prefill_causal_workspace_size(nq, n_kv, q_pos0, hq, hkv, d)
     ws, ws_bytes = _workspace(nbytes, q.device, workspace)
     st = lib().gqa_prefill_causal(_dev(q, torch.float16, "q"), _dev(k, torch.float16, "k", (n_kv, hkv, d)),
-                                  _dev(v, torch.float16, "v"), _dev(o, torch.float16, "o", q.shape), nq, n_kv, q_pos0, hq,
-                                  hkv,
-                                  d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
+                                  _dev(v, torch.float16, "v"), _dev(o, torch.float16, "o", q.shape), nq, n_kv, q_pos0,
+                                  hq, hkv, d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()), ws_bytes,
                                   _stream(stream))
     _check(st, "gqa_prefill_causal")
     return o
