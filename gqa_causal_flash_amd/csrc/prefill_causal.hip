@@ -337,24 +337,43 @@ __device__ __forceinline__ void issue_k8(rsrc_t rk, int tile, GQA_LDS char* kdst
   }
 }
 
-// V keys tile*64 .. +63 (E4M3): thread t holds 32 codes of key t/8, columns
-// 32(t%8) .. +31.
+// V keys tile*64 .. +63 (E4M3): thread t holds two 16-byte pieces of key
+// r = t/8, pieces a and a + 8 with a = 2k for k = t%8 < 4 and 2k - 7
+// otherwise (piece p = columns 16p .. 16p+15).  A piece decodes to fp16
+// chunks 2p and 2p + 1; odd rows load the two 8-byte halves of a piece in
+// swapped order, so register half 0 always holds chunk 2p + (r & 1).  With
+// that, every 16-lane pass of each 16-byte LDS write in store_v16 (two rows
+// of 8 lanes) lands on 16 distinct bank positions: the decoded tile is
+// written without bank conflicts, at no vector-instruction cost.
+__device__ __forceinline__ int v8_piece(int tid) {
+  const int k = tid & 7;
+  return k < 4 ? 2 * k : 2 * k - 7;
+}
 __device__ __forceinline__ void load_v8(rsrc_t rv, int tile, int tid, u4 (&raw)[2]) {
-  const uint32_t off = (uint32_t)tile * kTileBytes8 + (uint32_t)(tid >> 3) * kRowBytes8 + 32u * (uint32_t)(tid & 7);
-  raw[0] = __builtin_amdgcn_raw_buffer_load_b128(rv, off, 0, 0);
-  raw[1] = __builtin_amdgcn_raw_buffer_load_b128(rv, off + 16, 0, 0);
+  const int r = tid >> 3;
+  const uint32_t sw = 8u * (uint32_t)(r & 1);
+  const uint32_t row = (uint32_t)tile * kTileBytes8 + (uint32_t)r * kRowBytes8 + 16u * (uint32_t)v8_piece(tid);
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const u2 lo = __builtin_amdgcn_raw_buffer_load_b64(rv, row + 128u * i + sw, 0, 0);
+    const u2 hi = __builtin_amdgcn_raw_buffer_load_b64(rv, row + 128u * i + (8u - sw), 0, 0);
+    raw[i] = u4{lo[0], lo[1], hi[0], hi[1]};
+  }
 }
 
-// Decoded V of thread t into the fp16 tile: row r = t/8, logical fp16 chunks
-// 4(t%8) .. +3, each at its swizzled place c ^ 4(r%8).
+// Decoded V of thread t into the fp16 tile: piece a + 8i gives chunks
+// 2(a + 8i) + (r & 1) (register half 0) and the other chunk of the pair, each
+// at its swizzled place c ^ 4(r%8).
 __device__ __forceinline__ void store_v16(GQA_LDS char* vdst, int tid, const u4 (&raw)[2]) {
-  const int r = tid >> 3, c0 = 4 * (tid & 7);
-  u4 d[4];
-  decode16(raw[0], d[0], d[1]);
-  decode16(raw[1], d[2], d[3]);
+  const int r = tid >> 3, sw = r & 1;
+  const int c0 = 2 * v8_piece(tid);
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    *(GQA_LDS u4*)(vdst + r * kRowBytes + 16 * v_phys_chunk(c0 + j, r)) = d[j];
+  for (int i = 0; i < 2; ++i) {
+    u4 d0, d1;
+    decode16(raw[i], d0, d1);
+    *(GQA_LDS u4*)(vdst + r * kRowBytes + 16 * v_phys_chunk(c0 + 16 * i + sw, r)) = d0;
+    *(GQA_LDS u4*)(vdst + r * kRowBytes + 16 * v_phys_chunk(c0 + 16 * i + 1 - sw, r)) = d1;
+  }
 }
 
 // K fragment of product step si for keys 32kb .. 32kb+31 of the E4M3 tile:
