@@ -41,13 +41,12 @@ struct PrefillParams {
   const _Float16* v;
   _Float16* o;
   float* part;
-  long long total;
   int nrows;
   int kv_live;  // keys 0 .. kv_live-1 can be visible (q_pos0 + nq)
   int q_pos0;
   int nqb;
   int grid;
-  int split;  // key-split pieces per q-block (0: stream-K split)
+  int split;  // key-split pieces per q-block
   unsigned long long* clk;  // profiling: {shader cycles, wall ticks} accumulator, or null
   float* lse;               // per packed row log-sum-exp (natural log), or null
   const int* vdesc;         // varlen: block descriptors (see prefill_varlen_prepass), else null
@@ -222,36 +221,13 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
 template <class Run>
 __device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, Run run) {
   const int w = blockIdx.x;
-  if (p.split > 0) {
-    // q-blocks are dispatched last first: they are the longest, so the
-    // shortest pieces end the kernel
-    const int b = p.nqb - 1 - w / p.split, j = w % p.split;
-    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
-    const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
-    // the split never exceeds the shortest q-block's tile count, so lo < hi
-    run(b, lo, hi, p.split == 1, b * p.split + j);
-    return;
-  }
-  long long t0 = prefill_range_start(w, p.total, p.grid);
-  const long long t1 = prefill_range_start(w + 1, p.total, p.grid);
-  if (t0 >= t1) return;
-  int b = 0;
-  long long cb = 0;
-  for (;;) {
-    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
-    if (cb + nt > t0) break;
-    cb += nt;
-    ++b;
-  }
-  while (t0 < t1) {
-    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
-    const long long seg_end = cb + nt < t1 ? cb + nt : t1;
-    const int lo = (int)(t0 - cb), hi = (int)(seg_end - cb);
-    run(b, lo, hi, lo == 0 && hi == nt, w + b);
-    t0 = seg_end;
-    cb += nt;
-    ++b;
-  }
+  // q-blocks are dispatched last first: they are the longest, so the
+  // shortest pieces end the kernel
+  const int b = p.nqb - 1 - w / p.split, j = w % p.split;
+  const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+  const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
+  // the split never exceeds the shortest q-block's tile count, so lo < hi
+  run(b, lo, hi, p.split == 1, b * p.split + j);
 }
 
 template <int C, int W>
@@ -607,23 +583,11 @@ __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
   constexpr int kParts = kRowsPerBlock / kMergeRowsPerWG;
   const int b = blockIdx.x / kParts;
   const int part = blockIdx.x % kParts;
-  int w0, w1, slot0;
-  if (p.split > 0) {  // pieces of q-block b are slots b*split .. b*split + split - 1
-    w0 = 0;
-    w1 = p.split - 1;
-    slot0 = b * p.split;
-  } else {
-    long long cb = 0;
-    for (int i = 0; i < b; ++i) cb += prefill_block_tiles(i, p.nrows, p.q_pos0);
-    const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
-    w0 = prefill_owner(cb, p.total, p.grid);
-    w1 = prefill_owner(cb + nt - 1, p.total, p.grid);
-    slot0 = b;
-  }
-  if (w0 == w1) return;  // done whole by one workgroup, already written
+  // the pieces of q-block b are slots b*split .. b*split + split - 1 (the
+  // merge runs only when split > 1)
   const int tid = threadIdx.x;
   const int rl = part * kMergeRowsPerWG + tid % kMergeRowsPerWG;
-  merge_row(p, w0 + slot0, w1 + slot0, rl, tid / kMergeRowsPerWG, b * kRowsPerBlock + rl);
+  merge_row(p, b * p.split, b * p.split + p.split - 1, rl, tid / kMergeRowsPerWG, b * kRowsPerBlock + rl);
 }
 
 // ------------------------------------------------------------------ varlen
@@ -771,7 +735,6 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.v = (const _Float16*)v;
   p.o = (_Float16*)o;
   p.part = (float*)workspace;
-  p.total = s.total;
   p.nrows = s.nrows;
   p.kv_live = q_pos0 + nq;
   (void)n_kv;
@@ -807,7 +770,6 @@ hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* 
   p.v = (const _Float16*)v;
   p.o = (_Float16*)o;
   p.part = (float*)workspace;
-  p.total = s.total;
   p.nrows = s.nrows;
   p.kv_live = q_pos0 + nq;
   (void)n_kv;
@@ -857,7 +819,6 @@ hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void
   p.o = (_Float16*)o;
   p.part = (float*)(ws + varlen_part_offset(vs));
   p.part_bytes = (uint32_t)((size_t)vs.cap * vs.split * kPartialFloats * 4);
-  p.total = 0;
   p.nrows = 0;
   p.kv_live = 0;
   p.q_pos0 = 0;

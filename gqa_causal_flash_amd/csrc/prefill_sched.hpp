@@ -8,15 +8,12 @@
 //
 // A q-block is 256 consecutive packed rows (one workgroup, eight waves of 32).
 // Its key range is 0 .. pmax (the position of its last row), cut into 64-key
-// tiles.  Laying the q-blocks' tiles end to end gives a line of T tiles that
-// is split evenly over G workgroups (workgroup w takes tiles floor(wT/G) ..
-// floor((w+1)T/G) - 1).  Where a workgroup's range cuts a q-block, each piece
-// leaves an online-softmax partial (max, sum, unnormalised accumulator) that a
-// second kernel merges exactly by log-sum-exp -- the block partial plus exact
-// merge of the long-prefill page, with the split chosen for an even load on
-// all compute units.  The piece of q-block b done by workgroup w is stored in
-// partial slot w + b (unique: walking the line, every new piece starts at a
-// workgroup boundary, a q-block boundary or both).
+// tiles.  The tiles of every q-block are cut into `split` equal key ranges
+// (pieces); each piece runs as one workgroup and, when split > 1, leaves an
+// online-softmax partial (max, sum, unnormalised accumulator) that a second
+// kernel merges exactly by log-sum-exp -- the block partial plus exact merge
+// of the long-prefill page, with the split chosen for an even load on all
+// compute units.
 #pragma once
 
 #include <stdint.h>
@@ -30,15 +27,13 @@ constexpr int kRowsPerBlock = GQA_PREFILL_ROWS;  // packed rows per workgroup
 constexpr int kWGsPerCU = 1;                     // 128 KiB of LDS per workgroup
 constexpr int kTileKeys = 64;       // keys per K/V tile
 constexpr int kTargetGrid = 256;    // one workgroup per MI355X compute unit
-constexpr int kMinTilesPerWG = 16;
 
 struct PrefillSched {
-  int nrows;        // nq * hq
+  int nrows;   // nq * hq
   int q_pos0;
-  int nqb;          // number of q-blocks
-  long long total;  // T
-  int grid;         // G
-  int split;        // >0: key-split mode with this many pieces per q-block (see below)
+  int nqb;     // number of q-blocks
+  int split;   // pieces per q-block (see below)
+  int grid;    // nqb * split workgroups
 };
 
 __host__ __device__ inline int prefill_block_tiles(int b, int nrows, int q_pos0) {
@@ -48,77 +43,40 @@ __host__ __device__ inline int prefill_block_tiles(int b, int nrows, int q_pos0)
   return (pmax + kTileKeys) / kTileKeys;  // ceil((pmax + 1) / 64)
 }
 
-// First tile of workgroup w's range.
-__host__ __device__ inline long long prefill_range_start(int w, long long total, int grid) {
-  return (long long)w * total / grid;
-}
-
-// Workgroup whose range contains tile x.
-__host__ __device__ inline int prefill_owner(long long x, long long total, int grid) {
-  return (int)(((x + 1) * grid - 1) / total);
-}
-
-// Key-split mode (used when split > 0): q-block b's tiles are cut into `split`
-// equal key ranges, piece j = tiles floor(j n_b / split) .. floor((j+1) n_b /
-// split) - 1, and workgroup u = (nqb - 1 - b) * split + j runs piece j of
-// q-block b (the longest q-blocks, the last ones, go first).  With split
-// dividing 8, the round-robin placement of workgroup u on XCD u % 8 puts only
-// piece u % split on each XCD, so the 32 workgroups of an XCD stream the same
-// K/V range at the same pace and share that XCD's L2.  Piece j of q-block b
-// leaves its partial in slot b * split + j.
-#ifndef GQA_PREFILL_KEYSPLIT
-#define GQA_PREFILL_KEYSPLIT 1
-#endif
-
+// Piece j of q-block b is tiles floor(j n_b / split) .. floor((j+1) n_b /
+// split) - 1, and workgroup u = (nqb - 1 - b) * split + j runs it (the
+// longest q-blocks, the last ones, go first).  With split dividing 8, the
+// round-robin placement of workgroup u on XCD u % 8 puts only piece u % split
+// on each XCD, so the 32 workgroups of an XCD stream the same K/V range at
+// the same pace and share that XCD's L2.  Piece j of q-block b leaves its
+// partial in slot b * split + j.  The split is the smallest power of two
+// (<= 8) giving at least two workgroups per compute unit, and never more
+// pieces than the shortest q-block has tiles.
 inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
   PrefillSched s;
   s.nrows = nq * hq;
   s.q_pos0 = q_pos0;
   s.nqb = (s.nrows + kRowsPerBlock - 1) / kRowsPerBlock;
-  long long t = 0;
-  for (int b = 0; b < s.nqb; ++b) t += prefill_block_tiles(b, s.nrows, q_pos0);
-  s.total = t;
-  long long g = (t + kMinTilesPerWG - 1) / kMinTilesPerWG;
-  if (g < s.nqb) g = s.nqb;
-  if (g > kTargetGrid) g = kTargetGrid;
-  if (g > t) g = t;
-  s.grid = (int)g;
-  s.split = 0;
-  if (GQA_PREFILL_KEYSPLIT) {
-    // smallest power-of-two split (<= 8) giving at least two workgroups per compute unit,
-    // never more pieces than the shortest q-block has tiles
-    int minnt = 1 << 30;
-    for (int b = 0; b < s.nqb; ++b) {
-      const int nt = prefill_block_tiles(b, s.nrows, q_pos0);
-      if (nt < minnt) minnt = nt;
-    }
-    int sp = 1;
-    while (sp < 8 && (long long)s.nqb * sp < 2LL * kTargetGrid * kWGsPerCU && sp * 2 <= minnt) sp *= 2;
-    s.split = sp;
-    s.grid = s.nqb * sp;
+  int minnt = 1 << 30;
+  for (int b = 0; b < s.nqb; ++b) {
+    const int nt = prefill_block_tiles(b, s.nrows, q_pos0);
+    if (nt < minnt) minnt = nt;
   }
+  int sp = 1;
+  while (sp < 8 && (long long)s.nqb * sp < 2LL * kTargetGrid * kWGsPerCU && sp * 2 <= minnt) sp *= 2;
+  s.split = sp;
+  s.grid = s.nqb * sp;
   return s;
 }
 
 // Partial slot: fp32 acc [64 column quads][rows][4], then m [rows], then l [rows].
 constexpr size_t kPartialFloats = (size_t)kRowsPerBlock * 256 + 2 * kRowsPerBlock;
 
-// True when some q-block is cut between workgroups (its partials need merging).
-inline bool prefill_needs_merge(const PrefillSched& s) {
-  if (s.split > 0) return s.split > 1;
-  long long cb = 0;
-  for (int b = 0; b < s.nqb; ++b) {
-    const int nt = prefill_block_tiles(b, s.nrows, s.q_pos0);
-    if (prefill_owner(cb, s.total, s.grid) != prefill_owner(cb + nt - 1, s.total, s.grid)) return true;
-    cb += nt;
-  }
-  return false;
-}
+// True when the q-blocks are cut into pieces whose partials need merging.
+inline bool prefill_needs_merge(const PrefillSched& s) { return s.split > 1; }
 
 inline size_t prefill_workspace_bytes(const PrefillSched& s) {
-  if (!prefill_needs_merge(s)) return 0;
-  if (s.split > 0) return (size_t)s.grid * kPartialFloats * sizeof(float);
-  return (size_t)(s.grid + s.nqb) * kPartialFloats * sizeof(float);
+  return prefill_needs_merge(s) ? (size_t)s.grid * kPartialFloats * sizeof(float) : 0;
 }
 
 // Varlen prefill (a batch of sequences packed end to end): the q-blocks of
