@@ -165,7 +165,10 @@ gqa_status gqa_prefill_causal_varlen_skipped(const void* workspace, int32_t* cou
  *            kv_block_ids[qblock_offsets[b] .. qblock_offsets[b+1]-1]; block
  *            id x covers tokens x*kv_block_tokens .. x*kv_block_tokens +
  *            kv_block_tokens - 1.  Ids within a query block must be distinct;
- *            their order does not matter (the library sorts them by address).
+ *            their order does not change the result.  Selections of up to
+ *            2048 ids are sorted by cache address (a repeated id is then
+ *            dropped and counted, see below); longer ones are used in the
+ *            given order, where a repeated id is not detected and counts twice.
  *   Row r of block b sees token j iff j lies in a selected block of b,
  *   j <= q_pos0 + r and j < live_len.  A row that sees nothing outputs 0.
  *   requires q_pos0 >= 0, q_pos0 + nq <= live_len <= n_table * page_size;

@@ -104,6 +104,14 @@ def test_paged_saturated_matches_dense_causal():
     assert_parity(out, ref, "saturated")
 
 
+def test_paged_selection_longer_than_the_sort_is_taken_in_order():
+    """More than 2048 blocks in one query block: the prepass keeps the given (shuffled) order instead
+    of sorting; 128 rows at positions 12000.., every earlier block selected (about 3000 per block)."""
+    x = workloads.paged_sparse_inputs(select_tokens=64, tail=12000, seed=41, nq=128, n_pages=1024, saturate=True)
+    assert np.diff(x.qblock_offsets).min() > 2048
+    assert_parity(_gpu(x), _oracle(x), "3000-block selections")
+
+
 @pytest.mark.parametrize("select,tail", [(64, 0), (512, 1), (2048, 3)])
 def test_paged_page784_parity(select, tail):
     """The block-sparse selection over a page-784 cache (non-monotonic table of 784-token pages)."""
