@@ -128,54 +128,61 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     }
     if (bad) atomicAdd(&errs, bad);
     const int rmax = (npow + kPrepassThreads - 1) / kPrepassThreads;  // register slots in use
-    int buf = 0;
-    for (int k = 2; k <= npow; k <<= 1) {
-      for (int j = k >> 1; j > 0; j >>= 1) {
-        if (j >= kPrepassThreads) {
-          const int rj = j / kPrepassThreads;
+    // The stages are written for a compile-time count of slots in use, so
+    // that a stage issues the exchanges of all its slots before it waits.
+    auto sort_slots = [&](auto rmc) {
+      constexpr int RM = decltype(rmc)::value;
+      int buf = 0;
+      for (int k = 2; k <= npow; k <<= 1) {
+        for (int j = k >> 1; j > 0; j >>= 1) {
+          if (j >= kPrepassThreads) {
+            const int rj = j / kPrepassThreads;
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            const int rp = r ^ rj;
-            const int i = tid + kPrepassThreads * r;
-            if (rp > r && i < npow) {
-              const bool up = (i & k) == 0;
-              const unsigned long long a = kv[r], c = kv[rp];
-              if ((a > c) == up) {
-                kv[r] = c;
-                kv[rp] = a;
+            for (int r = 0; r < RM; ++r) {
+              const int rp = r ^ rj;
+              const int i = tid + kPrepassThreads * r;
+              if (rp > r && rp < RM) {
+                const bool up = (i & k) == 0;
+                const unsigned long long a = kv[r], c = kv[rp];
+                if ((a > c) == up) {
+                  kv[r] = c;
+                  kv[rp] = a;
+                }
               }
             }
-          }
-        } else if (j < 64) {
+          } else {
+            unsigned long long c[RM];
+            if (j < 64) {
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if (r >= rmax) break;
-            const int i = tid + kPrepassThreads * r;
-            const unsigned long long a = kv[r];
-            const unsigned long long c = __shfl_xor(a, j);
-            const bool up = (i & k) == 0;
-            const bool lo = (i & j) == 0;  // the lower index of the pair keeps the smaller key when ascending
-            kv[r] = (lo == up) ? (a < c ? a : c) : (a < c ? c : a);
-          }
-        } else {
-          unsigned long long* kb = buf ? keys2 : keys;
+              for (int r = 0; r < RM; ++r) c[r] = __shfl_xor(kv[r], j);
+            } else {
+              unsigned long long* kb = buf ? keys2 : keys;
 #pragma unroll
-          for (int r = 0; r < R; ++r)
-            if (r < rmax) kb[tid + kPrepassThreads * r] = kv[r];
-          __syncthreads();
+              for (int r = 0; r < RM; ++r) kb[tid + kPrepassThreads * r] = kv[r];
+              __syncthreads();
 #pragma unroll
-          for (int r = 0; r < R; ++r) {
-            if (r >= rmax) break;
-            const int i = tid + kPrepassThreads * r;
-            const unsigned long long a = kv[r], c = kb[i ^ j];
-            const bool up = (i & k) == 0;
-            const bool lo = (i & j) == 0;
-            kv[r] = (lo == up) ? (a < c ? a : c) : (a < c ? c : a);
+              for (int r = 0; r < RM; ++r) c[r] = kb[(tid + kPrepassThreads * r) ^ j];
+              buf ^= 1;
+            }
+#pragma unroll
+            for (int r = 0; r < RM; ++r) {
+              const int i = tid + kPrepassThreads * r;
+              const unsigned long long a = kv[r];
+              const bool up = (i & k) == 0;
+              const bool lo = (i & j) == 0;  // the lower index of the pair keeps the smaller key when ascending
+              kv[r] = (lo == up) ? (a < c[r] ? a : c[r]) : (a < c[r] ? c[r] : a);
+            }
           }
-          buf ^= 1;
         }
       }
-    }
+    };
+    static_assert(R == 4, "slot counts 1, 2 and 4");
+    if (rmax <= 1)
+      sort_slots(std::integral_constant<int, 1>{});
+    else if (rmax == 2)
+      sort_slots(std::integral_constant<int, 2>{});
+    else
+      sort_slots(std::integral_constant<int, 4>{});
 #pragma unroll
     for (int r = 0; r < R; ++r)
       if (r < rmax) keys[tid + kPrepassThreads * r] = kv[r];
