@@ -42,9 +42,28 @@ def _ws(nq, n_kv, q_pos0, hq=6, hkv=1, d=256):
     return st, out.value
 
 
+def _expected_prefill_workspace(nq, q_pos0, hq=6):
+    """The key-split rule restated: q-blocks of 256 packed rows, each cut into the smallest power of two
+    (at most 8) of key ranges that gives at least 512 pieces, never more than its shortest q-block has
+    64-key tiles; each piece of a split q-block leaves a 256-row fp32 partial (acc, m, l)."""
+    rows = nq * hq
+    nqb = -(-rows // 256)
+    tiles = [(q_pos0 + min((b + 1) * 256 - 1, rows - 1) // 6 + 64) // 64 for b in range(nqb)]
+    split = 1
+    while split < 8 and nqb * split < 512 and split * 2 <= min(tiles):
+        split *= 2
+    return 0 if split == 1 else nqb * split * (256 * 256 + 2 * 256) * 4
+
+
+@pytest.mark.parametrize("nq,n_kv,q_pos0", [(8000, 128000, 120000), (8000, 40000, 32000), (256, 40000, 39744),
+                                             (777, 2500, 1723), (7, 100, 93), (1, 64, 63), (300, 300, 0)])
+def test_prefill_workspace_follows_the_key_split(nq, n_kv, q_pos0):
+    assert _ws(nq, n_kv, q_pos0) == (g.GQA_OK, _expected_prefill_workspace(nq, q_pos0))
+
+
 def test_prefill_workspace_query():
     st, n = _ws(8000, 128000, 120000)
-    assert st == g.GQA_OK and n > 0
+    assert st == g.GQA_OK and n == 752 * 264192  # 188 q-blocks x 4 key ranges
     assert _ws(1, 1, 0) == (g.GQA_OK, 0)
     assert _ws(0, 10, 0)[0] == g.GQA_ERR_INVALID
     assert _ws(10, 10, 1)[0] == g.GQA_ERR_INVALID        # q_pos0 + nq > n_kv
