@@ -200,6 +200,31 @@ def test_varlen_rejects_before_launch(kw, status):
     assert _varlen(**kw) == status
 
 
+@pytest.mark.parametrize("batch,total_q", [(8, 27606), (8, 40000), (1, 300), (3, 1), (64, 64)])
+def test_varlen_workspace_follows_the_schedule(batch, total_q):
+    """Restated: at most cap = ceil(6 total_q / 256) + batch q-blocks, each cut into the smallest power of
+    two (at most 8) of key ranges giving 1024 pieces; a 16-byte header and 8 int32 per q-block, rounded
+    up to 256 bytes, then one 264192-byte partial per piece when the split is above 1."""
+    cap = -(-6 * total_q // 256) + batch
+    split = 1
+    while split < 8 and cap * split < 1024:
+        split *= 2
+    head = -(-(16 + cap * 8 * 4) // 256) * 256
+    n = ctypes.c_size_t()
+    assert g.lib().gqa_prefill_causal_varlen_workspace_size(batch, total_q, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
+    assert n.value == head + (cap * split * 264192 if split > 1 else 0)
+
+
+@pytest.mark.parametrize("nq,n_kv", [(1, 261888), (8, 262144), (4, 4096), (2, 100), (1, 1)])
+def test_verify_workspace_follows_the_schedule(nq, n_kv):
+    """Restated: one 64-row fp32 partial (66048 bytes) per workgroup, with ceil(n_kv / 32) tiles spread
+    at 8 or more per workgroup over between 1 and 512 workgroups."""
+    grid = min(512, max(1, -(-n_kv // 32) // 8))
+    n = ctypes.c_size_t()
+    assert g.lib().gqa_verify_fp8kv_workspace_size(nq, n_kv, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
+    assert n.value == grid * (64 * 256 + 2 * 64) * 4
+
+
 def test_varlen_workspace_query():
     n = ctypes.c_size_t()
     assert g.lib().gqa_prefill_causal_varlen_workspace_size(8, 40000, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
