@@ -132,6 +132,23 @@ def test_paged_rejects_before_launch(kw, status):
     assert _paged(**kw) == status
 
 
+@pytest.mark.parametrize("nq,n_ids", [(4096, 1000), (4096, 64 * 128), (4096, 64 * 512), (4096, 64 * 32),
+                                       (128, 6048), (64, 1)])
+def test_paged_workspace_follows_the_layout(nq, n_ids):
+    """Restated: a 16-byte header, three int32 per 64-token query block (rounded up to 16 bytes), 8 bytes
+    per id (rounded up to 256 bytes), then, when the average selection is longer than 32 blocks (2 pieces;
+    4 above 128), one fp32 partial of 128 rows (132096 bytes) per row group of 128 packed rows and piece."""
+    nqb = -(-nq // 64)
+    entries = -(-(16 + 12 * nqb) // 16) * 16
+    part = -(-(entries + 8 * max(n_ids, 1)) // 256) * 256
+    avg = n_ids // nqb
+    pieces = 1 if avg <= 32 else 2 if avg <= 128 else 4
+    slots = nqb * 3 * pieces if pieces > 1 else 0
+    n = ctypes.c_size_t()
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(nq, n_ids, 64, 4, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
+    assert n.value == part + slots * (128 * 256 + 2 * 128) * 4
+
+
 def test_paged_workspace_query():
     n = ctypes.c_size_t()
     assert g.lib().gqa_prefill_paged_sparse_workspace_size(4096, 1000, 64, 4, 6, 1, 256, ctypes.byref(n)) == 0
