@@ -30,7 +30,12 @@ written by `python bench.py --summarize-counters FETCH.csv WRITE.csv` from two
 rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
 `bench.py --steps S --warmup W --no-cpu-baseline --copy-calibration-mib M`.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+With --sweep it instead prints one JSON line per point of the long-prefill
+key sweep (Q = 8000 at the last positions of KV = 40000, 48000, ..., 128000),
+each with the step time, the main kernel's time, TFLOP/s and fraction of the
+fp16 peak, and the shader clock; the default single line is not printed then.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
 """
 
 from __future__ import annotations
@@ -57,6 +62,8 @@ PEAK_CLOCK_MHZ = 2400.0
 PEAK_HBM_GBS = 8000.0
 # The long-prefill page's candidate at this workload (V100, FP16): 100.20284 ms.
 PAGE_MS_Q8000_KV128000 = 100.20284
+# Its two printed points of the key sweep (Test Result; other points are not printed).
+PAGE_MS_SWEEP = {40000: 30.27579, 128000: PAGE_MS_Q8000_KV128000}
 
 
 TRAFFIC_TABLE = os.path.join(ROOT, "profiles", "hbm_traffic_per_launch.md")
@@ -182,6 +189,38 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
     return head + "\n".join(lines) + "\n"
 
 
+def summarize_sweep_trace(trace_csv: str, steps: int, warmup: int) -> str:
+    """Markdown table of prefill_causal_fwd / prefill_merge durations per point of the key sweep.
+
+    Reads a rocprofv3 --kernel-trace CSV of `bench.py --sweep --steps S --warmup W`: the sweep runs its
+    points in order (KV = 40000, 48000, ..., 128000), each with warmup + steps calls, so dispatch i of a
+    kernel belongs to point i // (warmup + steps).  The timed calls' kernel time is the average over the
+    last `steps` dispatches of each point."""
+    per = warmup + steps
+    points = (workloads.LONG_40K,) + workloads.SWEEP
+    dur = {"prefill_causal_fwd": [], "prefill_merge": []}
+    with open(trace_csv, newline="") as f:
+        for row in csv.DictReader(f):
+            for k in dur:
+                if f"::{k}" in row["Kernel_Name"]:
+                    dur[k].append(int(row["End_Timestamp"]) - int(row["Start_Timestamp"]))
+    for k, v in dur.items():
+        if len(v) != per * len(points):
+            raise SystemExit(f"{trace_csv}: {len(v)} dispatches of {k}, expected {per * len(points)}")
+    lines = ["| KV | q_pos0 | FLOP | `prefill_causal_fwd` avg of timed (ms) | min (ms) | TFLOP/s | fraction of "
+             f"{PEAK_F16_TFLOPS} | `prefill_merge` avg (us) |",
+             "|---|---|---|---|---|---|---|---|"]
+    for i, cfg in enumerate(points):
+        fwd = dur["prefill_causal_fwd"][i * per + warmup:(i + 1) * per]
+        mrg = dur["prefill_merge"][i * per + warmup:(i + 1) * per]
+        ms = sum(fwd) / len(fwd) / 1e6
+        fl = prefill_flops(cfg.nq, cfg.n_kv, cfg.q_pos0)
+        tf = fl / (ms * 1e-3) / 1e12
+        lines.append(f"| {cfg.n_kv} | {cfg.q_pos0} | {fl:.4e} | {ms:.4f} | {min(fwd) / 1e6:.4f} | {tf:.1f} | "
+                     f"{tf / PEAK_F16_TFLOPS:.4f} | {sum(mrg) / len(mrg) / 1e3:.1f} |")
+    return "\n".join(lines) + "\n"
+
+
 def prefill_flops(nq: int, n_kv: int, q_pos0: int, hq: int = 6, d: int = 256) -> float:
     p0, p1 = q_pos0, q_pos0 + nq - 1
     pairs = (p0 + 1 + p1 + 1) * nq // 2
@@ -239,6 +278,26 @@ def bench_prefill(cfg, steps, warmup, seed=0):
     ms, kms = time_steps(step, steps, warmup)
     flops = prefill_flops(cfg.nq, cfg.n_kv, cfg.q_pos0)
     return dict(ms=ms, kernel_ms=kms, flops=flops, host=(q, k, v), clock_mhz=time_steps.clock_mhz)
+
+
+def sweep_point(cfg, steps, warmup):
+    """One point of the key sweep: step and main-kernel times, TFLOP/s and fractions of the fp16 peak."""
+    r = bench_prefill(cfg, steps, warmup)
+    achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
+    clock = r["clock_mhz"]
+    page_ms = PAGE_MS_SWEEP.get(cfg.n_kv)
+    return {
+        "workload": prefill_workload(cfg.n_kv), "nq": cfg.nq, "n_kv": cfg.n_kv, "q_pos0": cfg.q_pos0,
+        "flops": r["flops"], "steps": steps, "warmup": warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "tflops_step": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
+        "kernel_ms": round(r["kernel_ms"], 4),
+        "tflops_kernel": round(achieved, 2),
+        "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+        "clock_mhz": round(clock, 1) if clock else None,
+        "frac_at_clock": round(achieved / (PEAK_F16_TFLOPS * clock / PEAK_CLOCK_MHZ), 4) if clock else None,
+        "page_ms_v100": page_ms,
+    }
 
 
 def cpu_baseline_prefill(cfg, host, seconds: float):
@@ -453,13 +512,23 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", type=int, default=workloads.HEADLINE.n_kv, help="key count of the prefill workload")
     ap.add_argument("--no-paths", action="store_true", help="skip the paged and verifier measurements")
+    ap.add_argument("--sweep", action="store_true",
+                    help="time the dense prefill at every point of the key sweep (KV = 40000, 48000..128000) and "
+                         "print one JSON line per point instead of the default line")
     ap.add_argument("--copy-calibration-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (3 times), as the known-size reference "
                          "for the FETCH_SIZE / WRITE_SIZE counters")
+    ap.add_argument("--summarize-sweep-trace", metavar="TRACE_CSV",
+                    help="print the per-point kernel times of a rocprofv3 --kernel-trace CSV of a --sweep run made "
+                         "with the given --steps/--warmup, and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-launch HBM traffic table from two rocprofv3 --pmc counter_collection.csv "
                          "files of a run made with the given --steps/--warmup/--kv/--copy-calibration-mib, and exit")
     args = ap.parse_args(argv)
+
+    if args.summarize_sweep_trace:
+        print(summarize_sweep_trace(args.summarize_sweep_trace, args.steps, args.warmup), end="")
+        return 0
 
     if args.summarize_counters:
         print(summarize_counters(*args.summarize_counters, steps=args.steps, warmup=args.warmup,
@@ -476,6 +545,11 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+
+    if args.sweep:
+        for cfg in (workloads.LONG_40K,) + workloads.SWEEP:
+            print(json.dumps(sweep_point(cfg, args.steps, args.warmup)), flush=True)
+        return 0
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib << 20

@@ -56,3 +56,31 @@ def test_committed_traffic_table_parses():
     # whether or not it is current, the committed table must be readable
     with open(bench.TRAFFIC_TABLE) as f:
         assert "kernel source digest:" in f.read()
+
+
+def test_summarize_sweep_trace_assigns_points_in_order(tmp_path):
+    """Dispatch i of a kernel belongs to sweep point i // (warmup + steps); only the timed ones are averaged."""
+    import workloads
+
+    points = (workloads.LONG_40K,) + workloads.SWEEP
+    warmup, steps = 1, 2
+    cols = ["Kernel_Name", "Start_Timestamp", "End_Timestamp"]
+    path = tmp_path / "trace.csv"
+    with open(path, "w", newline="") as f:
+        w = csv.DictWriter(f, fieldnames=cols)
+        w.writeheader()
+        t = 0
+        for i in range(len(points)):
+            for j in range(warmup + steps):
+                fwd = 10**9 if j < warmup else (i + 1) * 10**6 + j  # warm-up calls are slow and must be ignored
+                w.writerow({"Kernel_Name": _k("prefill_causal_fwd"), "Start_Timestamp": t, "End_Timestamp": t + fwd})
+                t += fwd
+                w.writerow({"Kernel_Name": _k("prefill_merge"), "Start_Timestamp": t, "End_Timestamp": t + 30000})
+                t += 30000
+    rows = bench.summarize_sweep_trace(str(path), steps=steps, warmup=warmup).splitlines()[2:]
+    assert len(rows) == len(points)
+    for i, (cfg, row) in enumerate(zip(points, rows)):
+        cells = [c.strip() for c in row.strip("|").split("|")]
+        assert int(cells[0]) == cfg.n_kv
+        assert float(cells[3]) == round(((i + 1) * 10**6 + 1.5) / 1e6, 4)  # mean of j = 1, 2
+        assert float(cells[7]) == 30.0

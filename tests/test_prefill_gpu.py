@@ -59,9 +59,10 @@ def test_prefill_deterministic():
     assert np.array_equal(a, b)
 
 
-@pytest.mark.parametrize("cfg", [workloads.LONG_40K, workloads.HEADLINE], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", (workloads.LONG_40K,) + workloads.SWEEP, ids=lambda c: c.name)
 def test_prefill_full_size_sampled_rows(cfg):
-    """Full-size long prefill in the benchmark's launch configuration, checked on sampled rows."""
+    """Full-size long prefill at every point of the key sweep (KV = 40000, 48000..128000, Q = 8000 at the
+    last positions) in the benchmark's launch configuration, checked on sampled rows."""
     q, k, v = workloads.causal_inputs(cfg.nq, cfg.n_kv, seed=0)
     out = _gpu(q, k, v, cfg.q_pos0)
     assert np.isfinite(out).all()
