@@ -73,6 +73,14 @@ def test_prefill_workspace_query():
     assert g.lib().gqa_prefill_causal_workspace_size(1, 1, 0, 6, 1, 256, None) == g.GQA_ERR_INVALID
 
 
+def test_prefill_sizes_stop_at_the_32_bit_buffer_range():
+    """Every tensor is reached through 32-bit byte offsets: K/V rows up to 2^32 - 1 bytes, Q/O likewise."""
+    assert _ws(1, 8388607, 8388606)[0] == g.GQA_OK                     # 8388607 keys x 512 B < 2^32
+    assert _ws(1, 8388608, 8388607)[0] == g.GQA_ERR_UNSUPPORTED        # 2^32 bytes of K
+    assert _ws(1398101, 1398101, 0)[0] == g.GQA_OK                     # 1398101 x 6 rows x 512 B < 2^32
+    assert _ws(1398102, 1398102, 0)[0] == g.GQA_ERR_UNSUPPORTED
+
+
 def _prefill(q=FAKE, k=FAKE, v=FAKE, o=FAKE, nq=8000, n_kv=128000, q_pos0=120000, hq=6, hkv=1, d=256,
              scale=0.0625, ws=None, ws_bytes=0):
     return g.lib().gqa_prefill_causal(q, k, v, o, nq, n_kv, q_pos0, hq, hkv, d, scale, ws, ws_bytes, None)
