@@ -87,3 +87,38 @@ def test_prefill_profiling_times_and_clock():
     assert np.array_equal(plain, profiled)
     assert n == 1 and ms > 0
     assert 300.0 < mhz < 3000.0, mhz
+
+
+def test_prefill_at_the_32_bit_key_limit():
+    """8388607 keys, the most whose K and V bytes fit 32-bit buffer offsets (2^32 - 512 bytes each),
+    with six query rows at the last positions.  K is zero except for its last 4096 keys, so each
+    row's keys split exactly into a prefix of equal scores (mean of V, log-sum-exp log(count): the
+    zero-K closed form) and a tail that the oracle evaluates; the two are merged by log-sum-exp.
+    V is random everywhere, so every key's row must be read from the right place."""
+    n_kv, nq, tail = 8388607, 6, 4096
+    q_pos0 = n_kv - nq
+    prefix = n_kv - tail
+    rng = np.random.default_rng(77)
+    q = workloads._normal16(rng, (nq, 6, 256))
+    k = np.zeros((n_kv, 1, 256), dtype=np.float16)
+    k[prefix:] = workloads._normal16(rng, (tail, 1, 256))
+    v = np.empty((n_kv, 1, 256), dtype=np.float16)
+    vsum = np.zeros(256, dtype=np.float64)
+    step = 1 << 19
+    for a in range(0, n_kv, step):
+        b = min(n_kv, a + step)
+        v[a:b] = workloads._normal16(rng, (b - a, 1, 256))
+        vsum += v[a:min(b, prefix), 0].astype(np.float64).sum(axis=0) if a < prefix else 0.0
+    print("[32-bit limit] inputs ready", flush=True)
+    out = _gpu(q, k, v, q_pos0)
+    print("[32-bit limit] GPU done", flush=True)
+
+    qf = q.reshape(nq * 6, 256)
+    pos = q_pos0 + np.repeat(np.arange(nq), 6)
+    vis = oracle.causal_visible(pos, np.arange(prefix, n_kv))
+    o_t, lse_t = oracle.attend(qf, k[prefix:, 0], v[prefix:, 0], vis, SCALE)
+    lse_p = np.log(prefix)
+    mx = np.maximum(lse_t, lse_p)
+    w_p, w_t = np.exp(lse_p - mx), np.exp(lse_t - mx)
+    ref = (w_p[:, None] * (vsum / prefix)[None, :] + w_t[:, None] * o_t) / (w_p + w_t)[:, None]
+    assert_parity(out.reshape(nq * 6, 256), ref, "n_kv=8388607 q=6")
