@@ -30,6 +30,8 @@ written by `python bench.py --summarize-counters FETCH.csv WRITE.csv` from two
 rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE) of
 `bench.py --steps S --warmup W --no-cpu-baseline --copy-calibration-mib M`.
 
+With --tiny it instead prints one such line for the tiny workload (Q = 256 at
+positions 768..1023 of KV = 1024, launch-bound at this size).
 With --sweep it instead prints one JSON line per point of the long-prefill
 key sweep (Q = 8000 at the last positions of KV = 40000, 48000, ..., 128000),
 each with the step time, the main kernel's time, TFLOP/s and fraction of the
@@ -72,8 +74,8 @@ PAGED_DENSE_PAGES = (16, 784)  # paged dense causal prefill: every block up to t
 VERIFY_QUERIES = (1, 2, 4, 8)  # 1: the single-row tail
 
 
-def prefill_workload(n_kv: int) -> str:
-    return f"causal_gqa_prefill_q8000_kv{n_kv}"
+def prefill_workload(n_kv: int, nq: int = 8000) -> str:
+    return f"causal_gqa_prefill_q{nq}_kv{n_kv}"
 
 
 def paged_workload(select_tokens: int, tail: int = 1) -> str:
@@ -281,13 +283,13 @@ def bench_prefill(cfg, steps, warmup, seed=0):
 
 
 def sweep_point(cfg, steps, warmup):
-    """One point of the key sweep: step and main-kernel times, TFLOP/s and fractions of the fp16 peak."""
+    """One dense prefill workload: step and main-kernel times, TFLOP/s and fractions of the fp16 peak."""
     r = bench_prefill(cfg, steps, warmup)
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
     clock = r["clock_mhz"]
     page_ms = PAGE_MS_SWEEP.get(cfg.n_kv)
     return {
-        "workload": prefill_workload(cfg.n_kv), "nq": cfg.nq, "n_kv": cfg.n_kv, "q_pos0": cfg.q_pos0,
+        "workload": prefill_workload(cfg.n_kv, cfg.nq), "nq": cfg.nq, "n_kv": cfg.n_kv, "q_pos0": cfg.q_pos0,
         "flops": r["flops"], "steps": steps, "warmup": warmup,
         "ms_per_step": round(r["ms"], 4),
         "tflops_step": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
@@ -512,6 +514,9 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", type=int, default=workloads.HEADLINE.n_kv, help="key count of the prefill workload")
     ap.add_argument("--no-paths", action="store_true", help="skip the paged and verifier measurements")
+    ap.add_argument("--tiny", action="store_true",
+                    help="time the dense prefill of the tiny workload (Q=256 at positions 768..1023 of KV=1024) "
+                         "and print one JSON line instead of the default line")
     ap.add_argument("--sweep", action="store_true",
                     help="time the dense prefill at every point of the key sweep (KV = 40000, 48000..128000) and "
                          "print one JSON line per point instead of the default line")
@@ -545,6 +550,10 @@ def main(argv=None):
     if not torch.cuda.is_available():
         print("bench.py: no GPU visible", file=sys.stderr)
         return 1
+
+    if args.tiny:
+        print(json.dumps(sweep_point(workloads.TINY, args.steps, args.warmup)), flush=True)
+        return 0
 
     if args.sweep:
         for cfg in (workloads.LONG_40K,) + workloads.SWEEP:
