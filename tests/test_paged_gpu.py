@@ -183,3 +183,27 @@ def test_paged_empty_selection_gives_zero_rows():
 def test_paged_deterministic():
     x = workloads.paged_sparse_inputs(select_tokens=2048, tail=3, seed=16)
     assert np.array_equal(_gpu(x), _gpu(x))
+
+
+def test_paged_pool_at_the_32_bit_limit():
+    """A page pool of 524287 pages of 16 tokens, the most whose K and V bytes fit 32-bit buffer offsets
+    (2^32 - 8192 bytes each).  The request's pages are placed at the top of the pool through the page
+    table, so every gathered row lies above 2^31 bytes; the result must equal the oracle on the same
+    logical cache held in a small pool."""
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    x = workloads.paged_sparse_inputs(select_tokens=512, tail=1, seed=31, nq=1024)
+    n_big = 524287
+    base = n_big - x.k_cache.shape[0]  # small page i lives at big page base + i
+    k_big = torch.zeros((n_big,) + x.k_cache.shape[1:], dtype=torch.float16, device="cuda")
+    v_big = torch.zeros_like(k_big)
+    k_big[base:] = to_dev(x.k_cache)
+    v_big[base:] = to_dev(x.v_cache)
+    table = (x.page_table.astype(np.int64) + base).astype(np.int32)
+    out, _ = g.gqa_prefill_paged_sparse(to_dev(x.q), k_big, v_big, to_dev(table), to_dev(x.qblock_offsets),
+                                        to_dev(x.kv_block_ids), x.q_pos0, x.live_len, x.scale)
+    res = to_host(out)
+    del k_big, v_big
+    assert_parity(res, _oracle(x), "pool of 524287 pages, request at the top")
