@@ -103,3 +103,28 @@ def test_varlen_benchmark_batch_sampled_rows():
                                              x.scale, rows=rows)
         assert_parity(o[q0 + rows], ref, f"request {i} (kv {nkv}, q {nq})")
         assert np.abs(lse[q0 + rows].astype(np.float64) - ref_lse).max() <= TOL_LSE, f"request {i} lse"
+
+
+def test_varlen_sequence_at_the_32_bit_key_limit():
+    """A packed key buffer of 8388607 rows, the most whose K and V bytes fit 32-bit buffer offsets: the
+    first sequence holds keys only (no queries), the second its 1024 keys at the very top of the buffer
+    with 256 queries.  The result must equal the dense oracle of the second sequence alone."""
+    import torch
+
+    import gqa_causal_flash_amd as g
+
+    total_kv, nkv, nq = 8388607, 1024, 256
+    q, k, v = workloads.causal_inputs(nq, nkv, seed=41)
+    k_big = torch.zeros((total_kv, 1, 256), dtype=torch.float16, device="cuda")
+    v_big = torch.zeros_like(k_big)
+    k_big[total_kv - nkv:] = to_dev(k)
+    v_big[total_kv - nkv:] = to_dev(v)
+    cu_q = np.array([0, 0, nq], dtype=np.int32)
+    cu_kv = np.array([0, total_kv - nkv, total_kv], dtype=np.int32)
+    o, lse, _ = g.gqa_prefill_causal_varlen(to_dev(q), k_big, v_big, to_dev(cu_q), to_dev(cu_kv), workloads.SCALE)
+    res, res_lse = to_host(o), lse.cpu().numpy()
+    del k_big, v_big
+    ref, ref_lse = oracle.prefill_causal(q, k, v, nkv - nq, workloads.SCALE)
+    assert_parity(res, ref, "varlen sequence at the top of 8388607 keys")
+    err = np.abs(res_lse.astype(np.float64) - ref_lse).max()
+    assert err <= TOL_LSE, f"lse error {err:.3e}"
