@@ -17,7 +17,9 @@ Prints ONE JSON line.  Besides the driver's fields it carries
                 fraction of the peak rescaled to that clock;
   cpu_baseline  the fp64 oracle timed on this host's cores for a bounded sample
                 of query rows of the same workload, in the same unit;
-  paths         the same measurement for the other entry points: the paged
+  paths         the same measurement for the other workloads: the tiny causal
+                prefill (Q = 256, KV = 1024), the KV = 40000 long prefill and the
+                other points of the key sweep (48000..120000), the paged
                 block-sparse prefill (S = 64/512/2048), the paged dense causal
                 prefill (every block selected, pages of 16 and 784 tokens), the
                 FP8 verifier tail (q = 2/4/8) and the varlen causal prefill of
@@ -155,7 +157,10 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
               "prefill_causal_e4m3": "e4m3"}
     first = {"prefill_causal_fwd", "paged_prepass", "verify_fwd", "prefill_varlen_prepass",
              "prefill_causal_e4m3"}  # a step starts here
-    labels = {"prefill": [prefill_workload(n_kv)], "varlen": [varlen_workload()], "e4m3": [e4m3_workload(128000)],
+    # the order in which main() runs the workloads of each family
+    prefill_paths = [workloads.TINY, workloads.LONG_40K] + [c for c in workloads.SWEEP if c.n_kv != n_kv]
+    labels = {"prefill": [prefill_workload(n_kv)] + [prefill_workload(c.n_kv, c.nq) for c in prefill_paths],
+              "varlen": [varlen_workload()], "e4m3": [e4m3_workload(128000)],
               "paged": [paged_workload(s) for s in PAGED_SELECTIONS] + [paged_dense_workload(p) for p in PAGED_DENSE_PAGES],
               "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
     true_kib = calib_mib * 1024.0
@@ -229,16 +234,23 @@ def prefill_flops(nq: int, n_kv: int, q_pos0: int, hq: int = 6, d: int = 256) ->
     return 4.0 * d * hq * pairs
 
 
-def _blas_threads() -> int:
+def host_cpu_model() -> str:
     try:
-        from threadpoolctl import threadpool_info
-
-        n = [i.get("num_threads", 0) for i in threadpool_info() if i.get("user_api") == "blas"]
-        if n:
-            return int(max(n))
-    except Exception:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
         pass
-    return len(os.sched_getaffinity(0))
+    return "unknown"
+
+
+def numpy_blas() -> str:
+    try:
+        blas = np.show_config(mode="dicts")["Build Dependencies"]["blas"]
+        return f"{blas.get('name', '?')} {blas.get('version', '')}".strip()
+    except Exception:
+        return "unknown"
 
 
 def time_steps(fn, steps: int, warmup: int):
@@ -288,8 +300,9 @@ def sweep_point(cfg, steps, warmup):
     achieved = r["flops"] / (r["kernel_ms"] * 1e-3) / 1e12
     clock = r["clock_mhz"]
     page_ms = PAGE_MS_SWEEP.get(cfg.n_kv)
+    name = prefill_workload(cfg.n_kv, cfg.nq)
     return {
-        "workload": prefill_workload(cfg.n_kv, cfg.nq), "nq": cfg.nq, "n_kv": cfg.n_kv, "q_pos0": cfg.q_pos0,
+        "workload": name, "nq": cfg.nq, "n_kv": cfg.n_kv, "q_pos0": cfg.q_pos0,
         "flops": r["flops"], "steps": steps, "warmup": warmup,
         "ms_per_step": round(r["ms"], 4),
         "tflops_step": round(r["flops"] / (r["ms"] * 1e-3) / 1e12, 2),
@@ -299,25 +312,37 @@ def sweep_point(cfg, steps, warmup):
         "clock_mhz": round(clock, 1) if clock else None,
         "frac_at_clock": round(achieved / (PEAK_F16_TFLOPS * clock / PEAK_CLOCK_MHZ), 4) if clock else None,
         "page_ms_v100": page_ms,
+        "roofline": {"kernel": "prefill_causal_fwd", "bound": "mfma", "achieved": round(achieved, 2),
+                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4),
+                     "algorithmic_bytes": prefill_bytes(cfg),
+                     "traffic": recorded_traffic().get(("prefill_causal_fwd", name))},
     }
 
 
+def prefill_bytes(cfg) -> int:
+    """Q, K, V and O of a dense prefill, each read or written once (fp16)."""
+    return 2 * (2 * cfg.nq * cfg.hq * cfg.d + 2 * cfg.n_kv * cfg.hkv * cfg.d)
+
+
 def cpu_baseline_prefill(cfg, host, seconds: float):
-    """fp64 oracle on a sample of query rows spread over the workload, timed on this host."""
-    import oracle
+    """fp64 oracle on a sample of query rows spread over the workload, timed on this host: one worker
+    process per host core (at most 16), each with single-threaded BLAS, each evaluating its share of the
+    sampled rows with the unchanged oracle function."""
+    from oracle import rowpool
 
     q, k, v = host
     rng = np.random.default_rng(7)
+    procs = rowpool.host_cores()
 
     def run(n):
         rows = np.sort(rng.choice(cfg.nq, n, replace=False))
         t0 = time.perf_counter()
-        oracle.prefill_causal(q, k, v, cfg.q_pos0, cfg.scale, rows=rows)
+        rowpool.run_rows("prefill_causal", (q, k, v, cfg.q_pos0, cfg.scale), rows=rows, procs=procs)
         dt = time.perf_counter() - t0
         pairs = int((cfg.q_pos0 + rows + 1).sum())
         return dt, pairs, n
 
-    n = 16
+    n = 8 * procs
     dt, pairs, n = run(n)
     for _ in range(4):  # grow the sample until it takes about `seconds`
         if dt >= 0.6 * seconds or n >= cfg.nq:
@@ -328,10 +353,14 @@ def cpu_baseline_prefill(cfg, host, seconds: float):
     return dict(
         value=flops / dt / 1e12,
         unit="TFLOP/s",
-        cores=_blas_threads(),
+        cores=procs,
         kind="oracle",
         sample=f"{n} of {cfg.nq} query rows (x{cfg.hq} heads, all visible keys of each, up to {cfg.n_kv}) "
-               f"in {dt:.1f} s of fp64 numpy/BLAS",
+               f"in {dt:.1f} s of fp64 numpy, {procs} worker processes with single-threaded BLAS "
+               f"(process start included)",
+        cpu_model=host_cpu_model(),
+        blas=numpy_blas(),
+        processes=procs,
     )
 
 
@@ -347,6 +376,40 @@ def paged_visible_pairs(x) -> int:
         pos = x.q_pos0 + np.arange(r0, r1)
         total += int(np.searchsorted(toks, pos, side="right").sum())
     return total
+
+
+def paged_bytes(x):
+    """(algorithmic, gathered) bytes of a paged workload.  Algorithmic: every live K and V row that some
+    query block selects, once (the union of the selections), plus Q and O.  Gathered: each query block's
+    selected live rows counted per query block (what the kernel copies to LDS), plus Q and O."""
+    ids = np.asarray(x.kv_block_ids, dtype=np.int64)
+    live = np.clip(x.live_len - 4 * ids, 0, 4)  # live tokens of each selected 4-token block
+    uniq = np.unique(ids)
+    live_u = np.clip(x.live_len - 4 * uniq, 0, 4)
+    row = 2 * 256 * 2  # one token of K and of V, fp16
+    qo = 2 * x.q.nbytes
+    return int(live_u.sum()) * row + qo, int(live.sum()) * row + qo
+
+
+def roofline_mfma_or_hbm(kernel: str, flops: float, nbytes: int, kms: float) -> dict:
+    """Roofline of a kernel that both multiplies and streams: the binding roof is the one whose time at
+    peak is longer (matrix cores at the fp16 peak, or HBM at 8 TB/s); `achieved` and `frac` are given
+    against it, and the other figure is kept beside it."""
+    t_mfma = flops / (PEAK_F16_TFLOPS * 1e12)
+    t_hbm = nbytes / (PEAK_HBM_GBS * 1e9)
+    tf = flops / (kms * 1e-3) / 1e12
+    gbs = nbytes / (kms * 1e-3) / 1e9
+    if t_hbm > t_mfma:
+        r = {"kernel": kernel, "bound": "hbm", "achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+             "frac": round(gbs / PEAK_HBM_GBS, 4), "tflops": round(tf, 2),
+             "frac_of_fp16_peak": round(tf / PEAK_F16_TFLOPS, 4)}
+    else:
+        r = {"kernel": kernel, "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS,
+             "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 4), "GBps": round(gbs, 1),
+             "frac_of_hbm_peak": round(gbs / PEAK_HBM_GBS, 4)}
+    r.update(algorithmic_bytes=int(nbytes), algorithmic_flops=flops,
+             us_at_mfma_peak=round(t_mfma * 1e6, 2), us_at_hbm_peak=round(t_hbm * 1e6, 2))
+    return r
 
 
 def bench_paged(select_tokens, steps, warmup, tail=1, seed=0, dense_page_size=None):
@@ -377,18 +440,14 @@ def bench_paged(select_tokens, steps, warmup, tail=1, seed=0, dense_page_size=No
     ms, kms = time_steps(step, steps, warmup)
     pairs = paged_visible_pairs(x)
     flops = 4.0 * 256 * 6 * pairs
-    # bytes the attention kernel moves: gathered K and V rows of every query block, Q and O
-    gathered = sum(max(0, int(min(x.live_len, 4 * (b + 1)) - 4 * b)) for b in x.kv_block_ids) * 2 * 512
-    moved = gathered + 2 * x.q.nbytes
-    tf = flops / (kms * 1e-3) / 1e12
+    alg, gathered = paged_bytes(x)
     line = {
         "workload": name,
         "ms_per_step": round(ms, 4), "kernel_ms": round(kms, 4),
         "tflops": round(flops / (ms * 1e-3) / 1e12, 2), "visible_pairs_per_head": pairs,
-        "roofline": {"kernel": "paged_fwd", "bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_F16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(tf / PEAK_F16_TFLOPS, 4),
-                     "moved_GBps": round(moved / (kms * 1e-3) / 1e9, 1),
-                     "traffic": recorded_traffic().get(("paged_fwd", name))},
+        "roofline": dict(roofline_mfma_or_hbm("paged_fwd", flops, alg, kms),
+                         gathered_bytes=gathered, gathered_GBps=round(gathered / (kms * 1e-3) / 1e9, 1),
+                         traffic=recorded_traffic().get(("paged_fwd", name))),
     }
     if dense_page_size is None:
         line["page_ms_v100"] = {64: 1.010, 512: 3.204, 2048: 11.203}[select_tokens]
@@ -602,12 +661,17 @@ def main(argv=None):
             "peak_at_clock": round(PEAK_F16_TFLOPS * r["clock_mhz"] / PEAK_CLOCK_MHZ, 1) if r["clock_mhz"] else None,
             "frac_at_clock": round(achieved / (PEAK_F16_TFLOPS * r["clock_mhz"] / PEAK_CLOCK_MHZ), 4)
             if r["clock_mhz"] else None,
-            "algorithmic_bytes": 2 * (2 * cfg.nq * cfg.hq * cfg.d + 2 * cfg.n_kv * cfg.d),
+            "algorithmic_bytes": prefill_bytes(cfg),
             "traffic": recorded_traffic().get(("prefill_causal_fwd", cfg.name)),
         },
     }
     if not args.no_paths:
         line["paths"] = {
+            # the tiny workload (Q = 256 at 768..1023 of KV = 1024), the page's KV = 40000 point and the rest of
+            # its key sweep (48000..120000; 128000 is the line's own workload)
+            "prefill_tiny": [sweep_point(workloads.TINY, args.steps, args.warmup)],
+            "prefill_long_40k": [sweep_point(workloads.LONG_40K, args.steps, args.warmup)],
+            "prefill_sweep": [sweep_point(c, args.steps, args.warmup) for c in workloads.SWEEP if c.n_kv != cfg.n_kv],
             "paged_sparse": [bench_paged(sel, args.steps, args.warmup) for sel in PAGED_SELECTIONS],
             "paged_dense": [bench_paged(None, args.steps, args.warmup, dense_page_size=ps) for ps in PAGED_DENSE_PAGES],
             "verify_fp8kv": [bench_verify(nq, args.steps, args.warmup) for nq in VERIFY_QUERIES],

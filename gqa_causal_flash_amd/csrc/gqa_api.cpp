@@ -277,7 +277,10 @@ gqa_status gqa_prefill_paged_sparse_workspace_size(int32_t nq, int32_t n_block_i
   gqa_status st = paged_sizes(nq, n_block_ids, qblock_rows, kv_block_tokens, hq, hkv, d);
   if (st != GQA_OK) return st;
   const int nqb = (nq + gqa::kQBlockTokens - 1) / gqa::kQBlockTokens;
-  *bytes = gqa::paged_layout(nqb, n_block_ids).total;
+  const size_t w = gqa::paged_layout(nqb, n_block_ids).total;
+  // the partials are addressed with 32-bit offsets from the workspace base
+  if ((int64_t)w > kMaxBufferBytes) return GQA_ERR_UNSUPPORTED;
+  *bytes = w;
   return GQA_OK;
 }
 
@@ -297,6 +300,8 @@ gqa_status gqa_prefill_paged_sparse(const void* q, const void* k_cache, const vo
   if (st != GQA_OK) return st;
   if (page_size % gqa::kBlockTokens != 0 || page_size > gqa::kMaxPageSize) return GQA_ERR_UNSUPPORTED;
   if ((int64_t)q_pos0 + nq > live_len || (int64_t)live_len > (int64_t)n_table * page_size) return GQA_ERR_INVALID;
+  // logical token positions (block id * 4) are int32 on the device
+  if ((int64_t)n_table * page_size > INT32_MAX) return GQA_ERR_UNSUPPORTED;
   // the cache buffer plus the out-of-range marker offset must fit 32 bits
   if ((int64_t)n_pages * page_size * hkv * d * 2 > 0xFFFFFF00ll) return GQA_ERR_UNSUPPORTED;
   if (!workspace || workspace_bytes < need) return GQA_ERR_WORKSPACE;

@@ -3,42 +3,73 @@
 import numpy as np
 
 # Parity bar for fp16 inputs with fp32 accumulation against the fp64 oracle:
-# max abs error 1e-3 beyond the rounding of the result to the fp16 output
-# format (unit roundoff 2^-11 of |O|, at most half an fp16 ulp), and relative
-# L2 error 5e-3 over the whole tensor.  The long-prefill page's 1e-3 envelope
-# (Test Result) compares two fp16 outputs, which share that rounding; against
-# the unrounded fp64 oracle it has to be allowed for explicitly, since an fp16
-# value of magnitude 2..4 is already up to 9.8e-4 from the exact result.
+# max abs error 1e-3 and relative L2 error 5e-3 over the whole tensor.
+#
+# The long-prefill page's 1e-3 envelope (Test Result) compares two fp16
+# outputs.  Max abs is therefore taken against the oracle rounded to fp16
+# (round to nearest even), max |O - fp16(O_ref)| <= 1e-3, while rel L2 and
+# cosine use the unrounded oracle.  Where one fp16 step is larger than 1e-3
+# (|O_ref| >= 2, step 2^-9 and up), a result within 1e-3 of the exact value
+# before its own final rounding can still land one step from fp16(O_ref); only
+# calls that may produce such rows (a row seeing a handful of keys) pass
+# ``fp16_step_exempt=True``, and for them those elements are held to the exact
+# form of the same bound instead: |O - O_ref| <= 1e-3 + half an fp16 step at
+# O_ref (the largest rounding error of an fp16 value there).
 TOL_MAX_ABS = 1e-3
 TOL_REL_L2 = 5e-3
-FP16_UNIT_ROUNDOFF = 2.0 ** -11
+FP16_STEP_LIMIT = 2.0  # |x| >= 2: one fp16 step (2^-9 or more) exceeds 1e-3
+
+
+def fp16_half_step(x):
+    """Half the spacing of fp16 values at x (the largest rounding error of an fp16 value there)."""
+    a = np.abs(np.asarray(x, dtype=np.float64))
+    _, e = np.frexp(np.where(a > 0, a, 2.0 ** -30))  # a = f * 2^e, f in [0.5, 1): spacing 2^(e - 11)
+    return np.maximum(np.ldexp(1.0, e - 12), 2.0 ** -25)  # subnormal spacing 2^-24
 
 
 def metrics(out, ref):
-    """max abs, mean abs, relative L2 (whole tensor) and cosine of out vs ref."""
+    """max abs against the fp16-rounded oracle, the exact-bound excess, mean abs,
+    relative L2 (whole tensor) and cosine of out vs ref."""
     o = np.asarray(out, dtype=np.float64)
     r = np.asarray(ref, dtype=np.float64)
+    if o.size == 0:
+        return dict(max_abs=0.0, max_abs_vs_fp16_ref=0.0, max_abs_vs_fp16_ref_below_2=0.0,
+                    max_abs_beyond_rounding=0.0, elements_at_or_above_2=0, ref_at_max_abs=0.0, mean_abs=0.0,
+                    rel_l2=0.0, cosine=1.0, finite=True)
     d = o - r
+    r16 = r.astype(np.float16).astype(np.float64)  # numpy rounds float64 -> float16 to nearest even
+    d16 = np.abs(o - r16)
+    small = np.abs(r16) < FP16_STEP_LIMIT
+    excess = np.abs(d) - fp16_half_step(r)
     nr = np.linalg.norm(r)
-    excess = np.abs(d) - FP16_UNIT_ROUNDOFF * np.abs(r)
-    i = int(np.argmax(np.abs(d))) if d.size else 0
+    i = int(np.argmax(d16))
     return dict(
-        max_abs=float(np.abs(d).max()) if d.size else 0.0,
-        max_abs_beyond_fp16_rounding=float(excess.max()) if d.size else 0.0,
-        ref_at_max_abs=float(r.reshape(-1)[i]) if d.size else 0.0,
-        mean_abs=float(np.abs(d).mean()) if d.size else 0.0,
+        max_abs=float(np.abs(d).max()),
+        max_abs_vs_fp16_ref=float(d16.max()),
+        max_abs_vs_fp16_ref_below_2=float(d16[small].max()) if small.any() else 0.0,
+        max_abs_beyond_rounding=float(excess.max()),
+        elements_at_or_above_2=int((~small).sum()),
+        ref_at_max_abs=float(r.reshape(-1)[i]),
+        mean_abs=float(np.abs(d).mean()),
         rel_l2=float(np.linalg.norm(d) / nr) if nr > 0 else float(np.linalg.norm(d)),
         cosine=float((o * r).sum() / (np.linalg.norm(o) * nr)) if nr > 0 else 1.0,
         finite=bool(np.isfinite(o).all()),
     )
 
 
-def assert_parity(out, ref, label=""):
+def assert_parity(out, ref, label="", fp16_step_exempt=False):
     m = metrics(out, ref)
     print(f"[parity] {label} {m}", flush=True)
     assert m["finite"], f"{label}: non-finite output"
-    assert m["max_abs_beyond_fp16_rounding"] <= TOL_MAX_ABS, (
-        f"{label}: max abs error beyond fp16 output rounding {m['max_abs_beyond_fp16_rounding']:.3e} > {TOL_MAX_ABS}")
+    if fp16_step_exempt:
+        assert m["max_abs_vs_fp16_ref_below_2"] <= TOL_MAX_ABS, (
+            f"{label}: max |O - fp16(O_ref)| where |O_ref| < 2 is {m['max_abs_vs_fp16_ref_below_2']:.3e} > {TOL_MAX_ABS}")
+        assert m["max_abs_beyond_rounding"] <= TOL_MAX_ABS, (
+            f"{label}: max |O - O_ref| beyond half an fp16 step is {m['max_abs_beyond_rounding']:.3e} > {TOL_MAX_ABS}")
+    else:
+        assert m["max_abs_vs_fp16_ref"] <= TOL_MAX_ABS, (
+            f"{label}: max |O - fp16(O_ref)| {m['max_abs_vs_fp16_ref']:.3e} > {TOL_MAX_ABS} "
+            f"(at O_ref = {m['ref_at_max_abs']:.4f})")
     assert m["rel_l2"] <= TOL_REL_L2, f"{label}: rel L2 {m['rel_l2']:.3e} > {TOL_REL_L2}"
     return m
 

@@ -135,6 +135,12 @@ def _paged(**kw):
     (dict(hq=8), g.GQA_ERR_UNSUPPORTED),
     (dict(), g.GQA_ERR_WORKSPACE),
     (dict(ws=FAKE, ws_bytes=64), g.GQA_ERR_WORKSPACE),
+    # 2^20 pages of 4096 tokens: logical positions past the int32 range
+    (dict(n_table=1 << 20, page_size=4096, n_pages=1), g.GQA_ERR_UNSUPPORTED),
+    (dict(n_table=(1 << 31) // 4096, page_size=4096, n_pages=1), g.GQA_ERR_UNSUPPORTED),  # exactly 2^31 tokens
+    (dict(n_table=(1 << 31) // 4096 - 1, page_size=4096, n_pages=1), g.GQA_ERR_WORKSPACE),  # just below: accepted
+    # partials past the 32-bit workspace range (200000 rows, 512 ids per query block: 4 pieces)
+    (dict(nq=200000, n_ids=3125 * 512, q_pos0=0, live_len=200000, n_table=12500), g.GQA_ERR_UNSUPPORTED),
 ])
 def test_paged_rejects_before_launch(kw, status):
     assert _paged(**kw) == status
@@ -155,6 +161,18 @@ def test_paged_workspace_follows_the_layout(nq, n_ids):
     n = ctypes.c_size_t()
     assert g.lib().gqa_prefill_paged_sparse_workspace_size(nq, n_ids, 64, 4, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
     assert n.value == part + slots * (128 * 256 + 2 * 128) * 4
+
+
+def test_paged_workspace_stops_at_the_32_bit_range():
+    """The partial slots are addressed with 32-bit byte offsets: a layout past 2^32 - 1 bytes is refused."""
+    n = ctypes.c_size_t()
+    # 200000 rows = 3125 query blocks, 512 ids each: 4 pieces, 37500 slots of 132096 bytes (4.95 GB)
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(200000, 3125 * 512, 64, 4, 6, 1, 256,
+                                                           ctypes.byref(n)) == g.GQA_ERR_UNSUPPORTED
+    # 100000 rows: 1563 query blocks, 18756 slots (2.48 GB) still fit
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(100000, 1563 * 512, 64, 4, 6, 1, 256,
+                                                           ctypes.byref(n)) == g.GQA_OK
+    assert 2.4e9 < n.value < 2 ** 32
 
 
 def test_paged_workspace_query():

@@ -1,11 +1,19 @@
 """GPU parity of gqa_prefill_paged_sparse against the fp64 oracle (through the C ABI)."""
 
+import functools
+
 import numpy as np
 import pytest
 
+import helpers
 import oracle
 import workloads
-from helpers import assert_parity, to_dev, to_host
+from helpers import to_dev, to_host
+
+# The first rows of a query block can see as few as one selected token, so outputs
+# with |O| >= 2 occur (one fp16 step there exceeds 1e-3);
+# those elements are held to 1e-3 beyond their own fp16 rounding (helpers.assert_parity).
+assert_parity = functools.partial(helpers.assert_parity, fp16_step_exempt=True)
 
 pytestmark = pytest.mark.gpu
 

@@ -1,11 +1,19 @@
 """GPU parity of gqa_prefill_causal_varlen (packed batch, per-row lse) against the fp64 oracle."""
 
+import functools
+
 import numpy as np
 import pytest
 
+import helpers
 import oracle
 import workloads
-from helpers import assert_parity, to_dev, to_host
+from helpers import to_dev, to_host
+
+# The first rows of a sequence that starts at position 0 see one to a few keys, so
+# outputs with |O| >= 2 occur (one fp16 step there exceeds 1e-3);
+# those elements are held to 1e-3 beyond their own fp16 rounding (helpers.assert_parity).
+assert_parity = functools.partial(helpers.assert_parity, fp16_step_exempt=True)
 
 pytestmark = pytest.mark.gpu
 
