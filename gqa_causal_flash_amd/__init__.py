@@ -13,7 +13,8 @@ from __future__ import annotations
 import ctypes
 import os
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
+# GQA_LIBRARY names another build of the same library (e.g. a sanitizer build of its host code)
+_LIB_PATH = os.environ.get("GQA_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgqa.so")
 _lib = None
 
 GQA_OK, GQA_ERR_INVALID, GQA_ERR_UNSUPPORTED, GQA_ERR_WORKSPACE, GQA_ERR_HIP = range(5)
