@@ -32,6 +32,7 @@ SIGNATURES = {
     "gqa_prefill_paged_sparse_dropped": (_i32, [_vp, _i32p, _vp]),
     "gqa_verify_fp8kv_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, _szp]),
     "gqa_verify_fp8kv": (_i32, [_vp, _vp, _vp, _f32, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp, _sz, _vp]),
+    "gqa_verify_fp8kv_noalloc": (_i32, [_vp, _vp, _vp, _f32, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _f32, _vp]),
     "gqa_prefill_causal_e4m3": (_i32, [_vp, _f32, _vp, _f32, _vp, _f32, _vp, _i32, _i32, _i32, _i32, _i32, _i32, _f32,
                                        _vp, _sz, _vp]),
     "gqa_prefill_causal_varlen_workspace_size": (_i32, [_i32, _i32, _i32, _i32, _i32, ctypes.POINTER(ctypes.c_size_t)]),
@@ -316,4 +317,24 @@ def gqa_verify_fp8kv(q, k_e4m3, v_e4m3, k_scale: float, v_scale: float, scale: f
                                 n_kv, hq, hkv, d, scale, None if ws is None else ctypes.c_void_p(ws.data_ptr()),
                                 ws_bytes, _stream(stream))
     _check(st, "gqa_verify_fp8kv")
+    return o
+
+
+def gqa_verify_fp8kv_noalloc(q, k_e4m3, v_e4m3, k_scale: float, v_scale: float, scale: float, o=None, stream=None):
+    """gqa_verify_fp8kv without a workspace: the library's fixed per-device scratch holds the partials, and the
+    C call allocates nothing (pass `o` to allocate nothing here either).  Calls on one device must not overlap."""
+    import torch
+
+    nq, hq, d = q.shape
+    n_kv, hkv, _ = k_e4m3.shape
+    if tuple(v_e4m3.shape) != tuple(k_e4m3.shape):
+        raise ValueError("k and v must have the same shape")
+    if o is None:
+        o = torch.empty_like(q)
+    st = lib().gqa_verify_fp8kv_noalloc(_dev(q, torch.float16, "q"),
+                                        _dev(k_e4m3, torch.uint8, "k_e4m3", (n_kv, hkv, d)),
+                                        _dev(v_e4m3, torch.uint8, "v_e4m3"), k_scale, v_scale,
+                                        _dev(o, torch.float16, "o", q.shape), nq, n_kv, hq, hkv, d, scale,
+                                        _stream(stream))
+    _check(st, "gqa_verify_fp8kv_noalloc")
     return o

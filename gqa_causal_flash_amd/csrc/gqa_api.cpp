@@ -356,4 +356,20 @@ gqa_status gqa_verify_fp8kv(const void* q, const uint8_t* k_e4m3, const uint8_t*
                                              (hipStream_t)stream));
 }
 
+gqa_status gqa_verify_fp8kv_noalloc(const void* q, const uint8_t* k_e4m3, const uint8_t* v_e4m3, float k_scale,
+                                    float v_scale, void* o, int32_t nq, int32_t n_kv, int32_t hq, int32_t hkv,
+                                    int32_t d, float scale, void* stream) {
+  if (!q || !k_e4m3 || !v_e4m3 || !o) return GQA_ERR_INVALID;
+  if (!good_scale(scale) || !good_scale(k_scale) || !good_scale(v_scale)) return GQA_ERR_INVALID;
+  size_t need = 0;
+  gqa_status st = gqa_verify_fp8kv_workspace_size(nq, n_kv, hq, hkv, d, &need);
+  if (st != GQA_OK) return st;
+  if (need > gqa::kVerifyScratchBytes) return GQA_ERR_UNSUPPORTED;
+  void* ws = nullptr;
+  hipError_t e = gqa::verify_scratch(&ws);
+  if (e != hipSuccess) return hip_status(e);
+  return hip_status(gqa::launch_verify_fp8kv(q, k_e4m3, v_e4m3, k_scale, v_scale, o, nq, n_kv, hq, scale, ws,
+                                             (hipStream_t)stream));
+}
+
 }  // extern "C"

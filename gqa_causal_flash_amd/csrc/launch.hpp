@@ -37,4 +37,8 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
 hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v, float k_scale, float v_scale,
                                void* o, int nq, int n_kv, int hq, float scale, void* workspace, hipStream_t stream);
 
+// Device address of the current device's fixed verifier scratch
+// (kVerifyScratchBytes), looked up on the first call on each device.
+hipError_t verify_scratch(void** ptr);
+
 }  // namespace gqa

@@ -32,6 +32,8 @@
 #include "launch.hpp"
 #include "verify_sched.hpp"
 
+#include <atomic>
+#include <mutex>
 #include <type_traits>
 
 namespace gqa {
@@ -398,6 +400,42 @@ hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_merge, dim3(p.nrows * 4), dim3(16 * kMergeLanes), 0, stream, p);
   return hipGetLastError();
+}
+
+// Scratch of gqa_verify_fp8kv_noalloc, for callers that cannot allocate: room
+// for the partial slots of the largest verifier schedule (512 slots of 64
+// rows).  Every device the library runs on holds its own copy from module load
+// until the process ends, and every such call on that device shares it.  The
+// forward kernel writes every slot row the merge reads, so nothing in it has
+// to start at zero.
+static __device__ __align__(256) unsigned char scratch[kVerifyScratchBytes];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+}  // namespace
+
+// Device address of the current device's copy of `scratch`, looked up once per
+// device (the name itself is only a host-side stand-in for the symbol).
+hipError_t verify_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (p == nullptr) {
+      e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+      if (e != hipSuccess) return e;
+      if (p == nullptr) return hipErrorInvalidSymbol;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *ptr = p;
+  return hipSuccess;
 }
 
 }  // namespace gqa

@@ -39,4 +39,7 @@ inline VerifySched verify_schedule(int nq, int n_kv, int hq) {
 
 inline size_t verify_workspace_bytes(const VerifySched& s) { return (size_t)s.grid * kVerifySlotFloats * 4; }
 
+// Workspace of the largest schedule (any nq <= 8, n_kv <= 262144): 33.8 MB.
+constexpr size_t kVerifyScratchBytes = (size_t)kVerifyMaxGrid * kVerifySlotFloats * 4;
+
 }  // namespace gqa

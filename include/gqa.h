@@ -1,7 +1,8 @@
 /*
  * libgqa -- causal grouped-query attention for AMD Instinct MI355X (gfx950).
  *
- * One operation, three entry points:
+ * One operation, with entry points for dense, E4M3, varlen and paged
+ * block-sparse causal prefill and for an FP8-cache verifier tail:
  *
  *   O = softmax(scale * Q K^T + mask) V
  *
@@ -23,7 +24,8 @@
  *    Calls are asynchronous: they enqueue kernels on `stream` and return; they
  *    never synchronise, never allocate device memory, and keep no state
  *    between calls, so concurrent calls on different streams are safe when
- *    their workspaces differ.
+ *    their workspaces differ.  (gqa_verify_fp8kv_noalloc instead uses a fixed
+ *    per-device scratch array that the library holds; see there.)
  *  - `workspace` is caller-provided device scratch of at least the size the
  *    matching *_workspace_size() query returns for the same arguments
  *    (NULL is allowed when that size is 0).  Its contents on entry do not
@@ -221,6 +223,28 @@ gqa_status gqa_verify_fp8kv_workspace_size(int32_t nq, int32_t n_kv, int32_t hq,
 gqa_status gqa_verify_fp8kv(const void* q, const uint8_t* k_e4m3, const uint8_t* v_e4m3, float k_scale,
                             float v_scale, void* o, int32_t nq, int32_t n_kv, int32_t hq, int32_t hkv, int32_t d,
                             float scale, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ *
+ * FP8 verifier tail without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).
+ *
+ * Same operation, arguments, requirements and errors as gqa_verify_fp8kv,
+ * without the workspace: the split-KV partials go to a fixed scratch array
+ * of 33,816,576 bytes (512 partial slots of 64 rows) that the library holds
+ * in device memory, one copy per device, from the library's load until the
+ * process ends.  Every valid call fits it (nq <= 8, n_kv <= 262144; anything
+ * larger is GQA_ERR_UNSUPPORTED as above).  The call allocates and frees
+ * nothing; on its first call on a device it looks up that device's copy of
+ * the array (a failure there is GQA_ERR_HIP).
+ *
+ * All calls on one device share that device's array and it keeps the last
+ * call's contents: calls that may run at the same time on one device (other
+ * streams, other threads) race on it and must be serialised by the caller.
+ * ------------------------------------------------------------------------ */
+gqa_status gqa_verify_fp8kv_noalloc(const void* q, const uint8_t* k_e4m3, const uint8_t* v_e4m3, float k_scale,
+                                    float v_scale, void* o, int32_t nq, int32_t n_kv, int32_t hq, int32_t hkv,
+                                    int32_t d, float scale, void* stream);
 
 /* ------------------------------------------------------------------------ *
  * Kernel timing (observability).

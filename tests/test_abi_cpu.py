@@ -206,6 +206,35 @@ def test_verify_rejects_before_launch(kw, status):
     assert _verify(**kw) == status
 
 
+@pytest.mark.parametrize("kw,status", [
+    (dict(k=None), g.GQA_ERR_INVALID),
+    (dict(o=None), g.GQA_ERR_INVALID),
+    (dict(ks=0.0), g.GQA_ERR_INVALID),
+    (dict(nq=0), g.GQA_ERR_INVALID),
+    (dict(nq=10, n_kv=5), g.GQA_ERR_INVALID),
+    (dict(nq=9), g.GQA_ERR_UNSUPPORTED),
+    (dict(n_kv=262145), g.GQA_ERR_UNSUPPORTED),
+    (dict(hq=8), g.GQA_ERR_UNSUPPORTED),
+])
+def test_verify_noalloc_rejects_before_launch(kw, status):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, ks=0.01, vs=0.01, o=FAKE, nq=8, n_kv=261888, hq=6, hkv=1, d=256, scale=0.0625)
+    a.update(kw)
+    assert g.lib().gqa_verify_fp8kv_noalloc(a["q"], a["k"], a["v"], a["ks"], a["vs"], a["o"], a["nq"], a["n_kv"],
+                                            a["hq"], a["hkv"], a["d"], a["scale"], None) == status
+
+
+def test_verify_noalloc_scratch_holds_every_valid_call():
+    """The fixed scratch (512 slots of 64 rows, 33,816,576 bytes) covers the workspace of every accepted
+    verifier call; the largest is nq = 8 at the 262144-token capability."""
+    n = ctypes.c_size_t()
+    worst = 0
+    for nq in range(1, 9):
+        for n_kv in (nq, 4096, 100000, 261888, 262144):
+            assert g.lib().gqa_verify_fp8kv_workspace_size(nq, n_kv, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
+            worst = max(worst, n.value)
+    assert worst == 512 * (64 * 256 + 2 * 64) * 4 == 33816576
+
+
 def test_paged_dropped_rejects_null():
     n = ctypes.c_int32()
     assert g.lib().gqa_prefill_paged_sparse_dropped(None, ctypes.byref(n), None) == g.GQA_ERR_INVALID
