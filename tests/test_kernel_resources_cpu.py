@@ -67,7 +67,9 @@ def _kernels_and_loops(asm: str):
     for line in asm.splitlines():
         fm = re.match(r"^(_Z\w+):", line)
         if fm:
-            func, in_loop = _demangle(fm.group(1)), False
+            # kernels live in the anonymous namespace; other labels (device variables) end the function
+            func = _demangle(fm.group(1)) if "_GLOBAL__N_1" in fm.group(1) else None
+            in_loop = False
             continue
         if re.match(r"^(\.LBB\w+:|; %bb\.\d+:)", line):
             in_loop = "Loop Header" in line or "in Loop:" in line
