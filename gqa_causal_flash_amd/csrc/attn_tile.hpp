@@ -26,24 +26,29 @@
 
 namespace gqa {
 
-// S^T[32 keys][32C rows] = K Q^T for keys 32kb .. 32kb+31 of the staged tile.
-template <int C>
-__device__ __forceinline__ void qk_32keys(uint32_t kaddr, int kb, const h8 (&qf)[C][16], f16x (&s)[C]) {
+#ifndef GQA_KPF
+#define GQA_KPF 4
+#endif
+#ifndef GQA_KPV
+#define GQA_KPV 2
+#endif
+
+// S^T[32 keys][32C rows] = K Q^T for the 32 keys whose fragment si (head-dim
+// columns 16si .. 16si+15) kfrag(si) reads.
+template <int C, int KPF, class KFrag>
+__device__ __forceinline__ void qk_32keys_f(KFrag kfrag, const h8 (&qf)[C][16], f16x (&s)[C]) {
 #pragma unroll
   for (int c = 0; c < C; ++c) s[c] = f16x{};
   {
     // K fragments run kPF steps ahead of the matrix cores
-#ifndef GQA_KPF
-#define GQA_KPF 4
-#endif
-    constexpr int kPF = GQA_KPF;
+    constexpr int kPF = KPF;
     h8 kf[kPF];
 #pragma unroll
-    for (int j = 0; j < kPF; ++j) kf[j] = read_k_frag(kaddr, kb, j);
+    for (int j = 0; j < kPF; ++j) kf[j] = kfrag(j);
 #pragma unroll
     for (int si = 0; si < 16; ++si) {
       const h8 a = kf[si % kPF];
-      if (si + kPF < 16) kf[si % kPF] = read_k_frag(kaddr, kb, si + kPF);
+      if (si + kPF < 16) kf[si % kPF] = kfrag(si + kPF);
 #pragma unroll
       for (int c = 0; c < C; ++c) s[c] = mfma(a, qf[c][si], s[c]);
     }
@@ -56,6 +61,12 @@ __device__ __forceinline__ void qk_32keys(uint32_t kaddr, int kb, const h8 (&qf)
     }
     __builtin_amdgcn_sched_group_barrier(0x008, C * kPF, 0);
   }
+}
+
+// S^T[32 keys][32C rows] = K Q^T for keys 32kb .. 32kb+31 of the staged tile.
+template <int C, int KPF = GQA_KPF>
+__device__ __forceinline__ void qk_32keys(uint32_t kaddr, int kb, const h8 (&qf)[C][16], f16x (&s)[C]) {
+  qk_32keys_f<C, KPF>([&](int si) { return read_k_frag(kaddr, kb, si); }, qf, s);
 }
 
 // Online-softmax update from the scores of 32 keys; returns P^T as fp16 B operands.
@@ -105,16 +116,13 @@ __device__ __forceinline__ void softmax_32keys(f16x (&s)[C], f16x (&acc)[C][8], 
 }
 
 // O^T[256 d][32C rows] += V^T[256 d][32 keys] P^T for keys 32kb .. 32kb+31 of the staged tile.
-template <int C>
+template <int C, int KPV = GQA_KPV>
 __device__ __forceinline__ void pv_32keys(const GQA_LDS char* vt, uint32_t bv, int kb, const h8 (&pk)[C][2],
                                           f16x (&acc)[C][8]) {
   {
     // V^T fragments (two transposed reads each) run kPV steps ahead; step st
     // is head-dim tile st / 2 and key half st % 2.
-#ifndef GQA_KPV
-#define GQA_KPV 2
-#endif
-    constexpr int kPV = GQA_KPV;
+    constexpr int kPV = KPV;
     h4 vlo[kPV], vhi[kPV];
 #pragma unroll
     for (int j = 0; j < kPV; ++j) {
@@ -144,15 +152,30 @@ __device__ __forceinline__ void pv_32keys(const GQA_LDS char* vt, uint32_t bv, i
   }
 }
 
-template <int C, class Visible>
+template <int C, class Visible, int KPF = GQA_KPF, int KPV = GQA_KPV>
 __device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char* vt, uint32_t bv, int kb,
                                               const h8 (&qf)[C][16], f16x (&acc)[C][8], float (&m)[C],
                                               float (&l)[C], float cscale, bool mask, Visible visible) {
   f16x s[C];
-  qk_32keys<C>(kaddr, kb, qf, s);
+  qk_32keys<C, KPF>(kaddr, kb, qf, s);
   h8 pk[C][2];
   softmax_32keys<C>(s, acc, m, l, cscale, mask, visible, pk);
-  pv_32keys<C>(vt, bv, kb, pk, acc);
+  pv_32keys<C, KPV>(vt, bv, kb, pk, acc);
+}
+
+// attend_32keys for the first 32 keys of a K tile named by its LDS pointer `kt`
+// (bk = k_lane_base of the lane): the fragment addresses keep the tile's
+// identity, so the compiler can tell the tile apart from LDS that loads are
+// landing in elsewhere.
+template <int C, class Visible, int KPF = GQA_KPF, int KPV = GQA_KPV>
+__device__ __forceinline__ void attend_32keys_p(const GQA_LDS char* kt, uint32_t bk, const GQA_LDS char* vt, uint32_t bv,
+                                                const h8 (&qf)[C][16], f16x (&acc)[C][8], float (&m)[C],
+                                                float (&l)[C], float cscale, bool mask, Visible visible) {
+  f16x s[C];
+  qk_32keys_f<C, KPF>([&](int si) { return *(const GQA_LDS h8*)(kt + (bk ^ (32u * (uint32_t)si))); }, qf, s);
+  h8 pk[C][2];
+  softmax_32keys<C>(s, acc, m, l, cscale, mask, visible, pk);
+  pv_32keys<C, KPV>(vt, bv, 0, pk, acc);
 }
 
 // Key index inside the 32-key block held by this lane's accumulator register vv.

@@ -28,22 +28,21 @@ constexpr int kPagedWGsPerQBlock = kQBlockRows / kPagedRowsPerWG;  // 3
 constexpr int kPagedMagic = 0x47514150;  // "PAQG"
 constexpr int kSortMax = 2048;           // selections up to this many blocks are sorted
 
-// The attention kernel cuts each query block's selection into `pieces` equal
-// runs of 32-key sub-tiles (more pieces for longer selections, so that the
-// whole chip is busy); with more than one piece every (row group, piece)
-// leaves a partial of 128 rows that a merge kernel combines.
-inline int paged_pieces(int nqb, int n_ids) {
-  const long long avg_blocks = nqb > 0 ? (long long)n_ids / nqb : 0;
-  if (avg_blocks <= 32) return 1;
-  if (avg_blocks <= 128) return 2;
-  return 4;
-}
+// The attention kernel cuts the work, sub-tiles of 32 keys of every query
+// block, into equal runs, each taken by a team of three workgroups (one per
+// 128-row group of the query block), 21 teams per XCD: 504 workgroups, two
+// per compute unit.  A team writes the query blocks it covers whole straight
+// to O; each of the two at its ends that it covers only in part leaves, per
+// row group, a partial of 128 rows (fp32 acc, m, l) in one of the workgroup's
+// two slots, which a merge kernel combines.
+constexpr int kPagedTeams = 168;  // 8 XCDs x 21 teams
+constexpr int kPagedGrid = 512;   // workgroup ids: 64 per XCD, 63 of them in teams
+constexpr int kPagedSlots = 2 * 3 * kPagedTeams;
 
 constexpr size_t kPagedSlotFloats = (size_t)kPagedRowsPerWG * 256 + 2 * kPagedRowsPerWG;
 
 struct PagedLayout {
   size_t err, beg, cnt, entries, part, total;
-  int pieces;
 };
 
 inline PagedLayout paged_layout(int nqb, int n_ids) {
@@ -53,9 +52,7 @@ inline PagedLayout paged_layout(int nqb, int n_ids) {
   L.cnt = L.beg + 4 * (size_t)nqb;
   L.entries = (L.cnt + 4 * (size_t)nqb + 15) / 16 * 16;
   L.part = (L.entries + 8 * (size_t)(n_ids > 0 ? n_ids : 1) + 255) / 256 * 256;
-  L.pieces = paged_pieces(nqb, n_ids);
-  const size_t slots = L.pieces > 1 ? (size_t)nqb * kPagedWGsPerQBlock * L.pieces : 0;
-  L.total = L.part + slots * kPagedSlotFloats * 4;
+  L.total = L.part + (size_t)kPagedSlots * kPagedSlotFloats * 4;
   return L;
 }
 

@@ -53,7 +53,6 @@ struct PagedParams {
   int n_table, n_pages, page_size, n_ids, nq, nrows, nqb, q_pos0, live_len;
   size_t off_err, off_beg, off_cnt, off_entries, off_part;
   uint32_t part_bytes;
-  int pieces;
   float c;
 };
 
@@ -229,6 +228,71 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
 // ------------------------------------------------------------------ attention
 constexpr int kSubKeys = 32;                     // keys per sub-tile = 8 blocks
 constexpr int kSubBytes = kSubKeys * kRowBytes;  // 16 KiB for K or V
+constexpr int kDeadToken = 0x7FFFFFFF;           // token of an entry that holds nothing live
+// s_waitcnt vmcnt(0) (other counters untouched) as an instruction the compiler
+// sees: its own wait insertion then knows that every load has landed
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+// Work units.  Query block b needs n_b = ceil(cnt[b] / 8) sub-tiles of 32
+// keys for each of its three row groups.  Column unit (b, x) is sub-tile x of
+// query block b, numbered query block by query block; the C column units are
+// cut into equal runs of `per` consecutive units, and each run goes to a team
+// of three workgroups, one per row group, which stream the same sub-tiles at
+// the same pace: the team runs on one XCD, so two of the three gathers of
+// every block come from that XCD's L2.  Every compute unit gets the same work
+// whatever the selection lengths.  A run covers the tail of one query block,
+// whole query blocks and the head of another: whole ones are written straight
+// to O, and the (at most two) cut ones leave a partial of the row group in the
+// workgroup's slots 2w (its first query block) and 2w + 1 (its last), with
+// w = 3 team + g, which paged_merge combines.
+__device__ __forceinline__ int paged_nsub(const int* cnt, int b) { return (cnt[b] + 7) >> 3; }
+
+struct PagedRun {
+  int per;     // column units per team
+  int total;   // all column units
+  int teams;   // teams with work
+};
+
+// Sum over query blocks, computed by each wave on its own (64 query blocks per step).
+__device__ __forceinline__ PagedRun paged_run(const int* cnt, int nqb, int lane) {
+  int t = 0;
+  for (int b0 = 0; b0 < nqb; b0 += 64) {
+    const int b = b0 + lane;
+    t += b < nqb ? paged_nsub(cnt, b) : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
+  PagedRun r;
+  r.total = __builtin_amdgcn_readfirstlane(t);
+  r.per = max((r.total + kPagedTeams - 1) / kPagedTeams, 2);
+  r.teams = (r.total + r.per - 1) / r.per;
+  return r;
+}
+
+// The query block holding column unit u and its first unit (u < total).
+__device__ __forceinline__ void paged_find(const int* cnt, int nqb, int lane, int u, int& qb, int& first) {
+  int base = 0;
+  for (int b0 = 0; b0 < nqb; b0 += 64) {
+    const int b = b0 + lane;
+    const int n = b < nqb ? paged_nsub(cnt, b) : 0;
+    int incl = n;  // inclusive prefix over the 64 lanes
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int y = __shfl_up(incl, d);
+      if (lane >= d) incl += y;
+    }
+    const unsigned long long hit = __ballot(base + incl > u);
+    if (hit) {
+      const int l = __builtin_ctzll(hit);
+      qb = b0 + l;
+      first = __builtin_amdgcn_readfirstlane(base + __shfl(incl - n, l));
+      return;
+    }
+    base = __builtin_amdgcn_readfirstlane(base + __shfl(incl, 63));
+  }
+  qb = nqb;
+  first = base;
+}
 
 // Wave w stages rows 8w .. 8w+7 of a 32-key sub-tile, i.e. entries 2w, 2w+1
 // of the sub-tile; copy i covers rows 8w+2i, 8w+2i+1 = tokens 2(i%2), 2(i%2)+1
@@ -242,14 +306,23 @@ struct SubEntries {
   int2 e[2];
 };
 
+// The entries are read through the scalar data cache (constant address
+// space, wave-uniform addresses): they land in scalar registers and are counted
+// by the scalar-memory counter, so waiting for them never waits for the
+// gathers in flight, whose counter is a separate one.
+typedef const __attribute__((address_space(4))) int* const_int_ptr;
+
 __device__ __forceinline__ SubEntries sub_entries(const int2* ent, int e0, int e_end, int wave) {
+  const const_int_ptr cent = (const_int_ptr)(uintptr_t)ent;
   SubEntries s;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
     const int e = e0 + 2 * wave + k;  // wave-uniform
-    const int2 x = e < e_end ? ent[e] : int2{-1, 0x7FFFFFFF};
-    // uniform values: kept in scalar registers
-    s.e[k] = int2{__builtin_amdgcn_readfirstlane(x.x), __builtin_amdgcn_readfirstlane(x.y)};
+    if (e < e_end) {
+      s.e[k] = int2{cent[2 * e], cent[2 * e + 1]};
+    } else {
+      s.e[k] = int2{-1, 0x7FFFFFFF};
+    }
   }
   return s;
 }
@@ -279,24 +352,20 @@ __device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk,
   }
 }
 
-// Workgroup id -> (query block, row group, piece).  Ids u with the same u % 8
-// run on the same XCD, so every workgroup of one query block is given the same
-// u % 8 and its gathered K/V rows are shared through that XCD's L2.
-__device__ __forceinline__ bool paged_unit(int u, int nqb, int pieces, int& b, int& g, int& j) {
-  const int per_block = kPagedWGsPerQBlock * pieces;
-  const int x = u & 7, rest = u >> 3;
-  b = (rest / per_block) * 8 + x;
-  const int within = rest % per_block;
-  g = within / pieces;
-  j = within % pieces;
-  return b < nqb;
-}
-
 __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
-  __shared__ __attribute__((aligned(1024))) char smem[4 * kSubBytes];  // V 0/16 KiB, K 32/48 KiB
-  __shared__ __attribute__((aligned(16))) int kpos_s[2][kSubKeys];
-  int b, g, pj;
-  if (!paged_unit(blockIdx.x, p.nqb, p.pieces, b, g, pj)) return;
+  // two slots (K at 0, V at 16 KiB of a slot's array) and two position
+  // arrays, each its own array, and the loop below unrolled over the two
+  // slots: every LDS access names its array at compile time, so the compiler
+  // can tell that reading one slot does not touch the gather landing in the
+  // other, and inserts no wait for that gather
+  __shared__ __attribute__((aligned(1024))) char s0a[2 * kSubBytes];
+  __shared__ __attribute__((aligned(1024))) char s1a[2 * kSubBytes];
+  __shared__ __attribute__((aligned(16))) int kp0s[kSubKeys];
+  __shared__ __attribute__((aligned(16))) int kp1s[kSubKeys];
+  auto kslot = [&](auto sc) -> char* { return decltype(sc)::value ? s1a : s0a; };
+  auto vslot = [&](auto sc) -> char* { return kslot(sc) + kSubBytes; };
+  auto pslot = [&](auto sc) -> int* { return decltype(sc)::value ? kp1s : kp0s; };
+
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -304,107 +373,181 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   const int col = lane & 31;
   const uint32_t kl = 512u * half + 16u * (uint32_t)(col ^ half);
   const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
-
-  const int* cntp = (const int*)(p.ws + p.off_cnt);
+  const int* cnt = (const int*)(p.ws + p.off_cnt);
   const int* begp = (const int*)(p.ws + p.off_beg);
   const int2* ent = (const int2*)(p.ws + p.off_entries);
-  const int n = cntp[b];
-  const int e_beg = begp[b];
-  const int e_end = e_beg + n;
-  const int n_sub = (n + 7) / 8;
-  const int s_lo = (int)((long long)pj * n_sub / p.pieces);
-  const int s_hi = (int)((long long)(pj + 1) * n_sub / p.pieces);
+  const PagedRun run = paged_run(cnt, p.nqb, lane);
+  // Workgroup ids are dealt to the 8 XCDs in turn; an XCD's 64 ids hold 21
+  // teams of three.  The teams with work are cut into 8 contiguous groups, one
+  // per XCD, so that every XCD gets an equal share however few teams there are.
+  const int per_xcd = (run.teams + 7) / 8;
+  const int xi = blockIdx.x >> 3;
+  if (xi >= 3 * per_xcd) return;
+  const int team = (blockIdx.x & 7) * per_xcd + xi / 3;
+  const int g = xi % 3;  // this workgroup's row group
+  const int w = 3 * team + g;
+  int u = team * run.per;
+  const int u_end = min(run.total, u + run.per);
+  if (u >= u_end) return;
+  int b, first;
+  paged_find(cnt, p.nqb, lane, u, b, first);
 
   const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
   const uint32_t cache_bytes = (uint32_t)p.n_pages * (uint32_t)p.page_size * kRowBytes;
   const rsrc_t rk = make_rsrc(p.kc, cache_bytes);
   const rsrc_t rv = make_rsrc(p.vc, cache_bytes);
-
-  const int row_local = 32 * wave + col;  // row inside the 128-row group
-  const int row = b * kQBlockRows + g * kPagedRowsPerWG + row_local;
-  const int pos = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
-  h8 qf[1][16];
-  {
-    const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
-#pragma unroll
-    for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
-  }
-  f16x acc[1][8];
-#pragma unroll
-  for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
-  float m[1] = {-INFINITY}, l[1] = {0.f};
   uint32_t bk = k_lane_base(lane);
   uint32_t bv = v_lane_base(lane);
 
-  auto issue = [&](int x, const SubEntries& se) {
-    const int buf = x & 1;
-    paged_issue_sub(p, rk, rv, se, smem + (2 + buf) * kSubBytes, smem + buf * kSubBytes, kpos_s[buf], wave, lane, kl,
-                    vl);
-  };
-  SubEntries nxt = sub_entries(ent, e_beg + 8 * s_lo, e_end, wave);
-  if (s_lo < s_hi) issue(s_lo, nxt);
-  nxt = sub_entries(ent, e_beg + 8 * (s_lo + 1), e_end, wave);
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-  __syncthreads();
-  for (int x = s_lo; x < s_hi; ++x) {
-    const int buf = (x - s_lo) & 1;
-    if (x + 1 < s_hi) issue(x + 1, nxt);  // lands in the other slot
-    nxt = sub_entries(ent, e_beg + 8 * (x + 2), e_end, wave);  // in flight during this sub-tile
-    asm volatile("" : "+v"(bk), "+v"(bv));
-    int kp[16];
-#pragma unroll
-    for (int q4 = 0; q4 < 4; ++q4) {
-      const int4 v4 = *(const int4*)&kpos_s[(x & 1)][8 * q4 + 4 * half];
-      kp[4 * q4] = v4.x;
-      kp[4 * q4 + 1] = v4.y;
-      kp[4 * q4 + 2] = v4.z;
-      kp[4 * q4 + 3] = v4.w;
-    }
-    (void)buf;
-    attend_32keys<1>(lds_addr((const GQA_LDS char*)smem + (2 + (x & 1)) * kSubBytes) + bk,
-                     (const GQA_LDS char*)smem + (x & 1) * kSubBytes, bv, 0, qf, acc, m, l, p.c, true,
-                     [&](int, int vv) { return kp[vv] <= pos; });
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
+  bool first_seg = true;
+  while (u < u_end) {
+    // the segment: sub-tiles s0 .. s1-1 of row group g of query block b (all
+    // wave-uniform: kept in scalar registers)
+    const int count = __builtin_amdgcn_readfirstlane(cnt[b]);
+    const int nb = (count + 7) >> 3;
+    const int s0 = u - first;
+    const int s1 = min(nb, s0 + (u_end - u));
+    const int e_beg = __builtin_amdgcn_readfirstlane(begp[b]);
+    const int e_end = e_beg + count;
 
-  const float lt = swap_halves_sum(l[0]);
-  if (p.pieces == 1) {
-    // rows of a short last query block that fall past the end are not written
-    const int row_end = min(p.nrows, (b + 1) * kQBlockRows);
-    const rsrc_t ro = make_rsrc(p.o, (uint32_t)row_end * kRowBytes);
-    store_rows_f16(ro, row, half, acc[0], lt, 1.0f);
-  } else {
-    const rsrc_t rp = make_rsrc(p.ws + p.off_part, p.part_bytes);
-    const int slot = ((b * kPagedWGsPerQBlock) + g) * p.pieces + pj;
-    store_partial(rp, (uint32_t)slot * (uint32_t)(kPagedSlotFloats * 4), kPagedRowsPerWG, row_local, half, acc[0],
-                  m[0], lt);
+    const int row_local = 32 * wave + col;  // row inside the 128-row group
+    const int row_base = b * kQBlockRows + g * kPagedRowsPerWG + 32 * wave;
+    const int row = row_base + col;
+    const int pos = p.q_pos0 + min(row, p.nrows - 1) / kGroup;
+    const int wpos_lo = p.q_pos0 + min(row_base, p.nrows - 1) / kGroup;  // the wave's first row
+    h8 qf[1][16];
+    {
+      const uint32_t qoff = (uint32_t)row * kRowBytes + half * 16;
+#pragma unroll
+      for (int s = 0; s < 16; ++s) qf[0][s] = load_16B(rq, qoff + s * 32);
+    }
+    f16x acc[1][8];
+#pragma unroll
+    for (int dt = 0; dt < 8; ++dt) acc[0][dt] = f16x{};
+    float m[1] = {-INFINITY}, l[1] = {0.f};
+
+    auto issue = [&](auto sc, const SubEntries& se) {
+      paged_issue_sub(p, rk, rv, se, kslot(sc), vslot(sc), pslot(sc), wave, lane, kl, vl);
+    };
+    // Sub-tile x (i = x - s0) sits in slot i % 2, the gather of x + 1 is in
+    // flight while x is computed.  The entries of x are loaded into set i % 2
+    // two steps before the step that gathers with them (step x - 1), so a
+    // gather never waits for its entries.
+    SubEntries es[2];
+    es[0] = sub_entries(ent, e_beg + 8 * s0, e_end, wave);
+    issue(std::integral_constant<int, 0>{}, es[0]);
+    es[1] = sub_entries(ent, e_beg + 8 * (s0 + 1), e_end, wave);
+    es[0] = sub_entries(ent, e_beg + 8 * (s0 + 2), e_end, wave);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_barrier();
+    auto step = [&](auto ic, int x) {
+      constexpr int I = decltype(ic)::value;  // (x - s0) % 2
+      if (x + 1 < s1) issue(std::integral_constant<int, I ^ 1>{}, es[I ^ 1]);  // lands in the other slot
+      es[I ^ 1] = sub_entries(ent, e_beg + 8 * (x + 3), e_end, wave);          // used two steps on
+      // keep the per-lane bases opaque so derived addresses are formed here,
+      // next to their use, instead of being hoisted and held in registers
+      asm volatile("" : "+v"(bk), "+v"(bv));
+      const int* kps = pslot(std::integral_constant<int, I>{});
+      // a sub-tile whose keys all sit at or before the wave's first row (the
+      // usual case: selections lie mostly far behind the query block) needs no
+      // mask; dead and stale slots carry INT32_MAX and force one.  Positions of
+      // this lane's keys: 4 runs of 4 at 8q + 4h.
+      int kmax = -1;
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) {
+        const int4 v4 = *(const int4*)&kps[8 * q4 + 4 * half];
+        kmax = max(kmax, max(max(v4.x, v4.y), max(v4.z, v4.w)));
+      }
+      const bool mask = !__all(kmax <= wpos_lo);
+      auto visible = [&](int, int vv) { return kps[8 * (vv >> 2) + 4 * half + (vv & 3)] <= pos; };
+      // two K fragments in flight instead of four: the registers go to the
+      // schedule state, and no value of the loop is spilled
+      attend_32keys_p<1, decltype(visible), 2, 2>((const GQA_LDS char*)kslot(std::integral_constant<int, I>{}), bk,
+                                                  (const GQA_LDS char*)vslot(std::integral_constant<int, I>{}), bv, qf,
+                                                  acc, m, l, p.c, mask, visible);
+      // the gather into the other slot has landed and every wave is done with
+      // this one (a barrier without a memory fence: the wait is explicit)
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      lds_barrier();
+    };
+    for (int x = s0; x < s1; x += 2) {
+      step(std::integral_constant<int, 0>{}, x);
+      if (x + 1 < s1) step(std::integral_constant<int, 1>{}, x + 1);
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    const float lt = swap_halves_sum(l[0]);
+    if (s0 == 0 && s1 == nb) {
+      // rows past the last query row are dropped by the range check
+      const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+      store_rows_f16(ro, row, half, acc[0], lt, 1.0f);
+    } else {
+      const rsrc_t rp = make_rsrc(p.ws + p.off_part, p.part_bytes);
+      const int slot = 2 * w + (first_seg ? 0 : 1);
+      store_partial(rp, (uint32_t)slot * (uint32_t)(kPagedSlotFloats * 4), kPagedRowsPerWG, row_local, half, acc[0],
+                    m[0], lt);
+    }
+    first_seg = false;
+    u += s1 - s0;
+    if (u >= u_end) break;
+    // next query block; those with nothing selected hold no units
+    first += nb;
+    ++b;
+    while (b < p.nqb && __builtin_amdgcn_readfirstlane(cnt[b]) == 0) ++b;
   }
 }
 
-// Merge of the pieces of each 128-row group: workgroup (group, half) takes 64
-// rows; thread (row, 64 columns).
+// Merge of the cut row groups: workgroup (row group, half) takes 64 rows;
+// thread (row, 64 columns).  Query block b holds column units first_b ..
+// first_b + n_b - 1; the teams t_a = first_b / per .. t_b = (first_b + n_b - 1)
+// / per cover it.  One team means its row groups were written whole;
+// otherwise the row-group-g workgroup of team t_a contributes slot 2w (if b is
+// its first query block) or 2w + 1, and that of every later team slot 2w
+// (w = 3 team + g).  A query block with nothing selected is written as zeros.
 __global__ __launch_bounds__(256) void paged_merge(PagedParams p) {
   const int group = blockIdx.x >> 1;  // = b * 3 + g
+  const int b = group / kPagedWGsPerQBlock, g = group % kPagedWGsPerQBlock;
   const int rl = (blockIdx.x & 1) * 64 + (threadIdx.x & 63);
   const int dq = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
   const int row = group * kPagedRowsPerWG + rl;
-  const int b = group / kPagedWGsPerQBlock;
+  const int* cnt = (const int*)(p.ws + p.off_cnt);
+  const PagedRun run = paged_run(cnt, p.nqb, lane);
+  // first column unit of query block b: the sum over the blocks before it
+  int before = 0;
+  for (int b0 = 0; b0 < b; b0 += 64) {
+    const int bb = b0 + lane;
+    before += bb < b ? paged_nsub(cnt, bb) : 0;
+  }
+#pragma unroll
+  for (int d = 32; d >= 1; d >>= 1) before += __shfl_xor(before, d);
   if (row >= min(p.nrows, (b + 1) * kQBlockRows)) return;
+  const int nb = paged_nsub(cnt, b);
+  const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
+  const uint32_t obase = (uint32_t)row * kRowBytes + 128 * dq;
+  if (nb == 0) {
+#pragma unroll
+    for (int q = 0; q < 16; q += 2) store_16B(ro, obase + q * 8, u4{0u, 0u, 0u, 0u});
+    return;
+  }
+  const int fr = before;
+  const int wa = fr / run.per, wb = (fr + nb - 1) / run.per;  // teams
+  if (wa == wb) return;
   const rsrc_t rp = make_rsrc(p.ws + p.off_part, p.part_bytes);
   const uint32_t slot_bytes = (uint32_t)(kPagedSlotFloats * 4);
   const uint32_t m_off = (uint32_t)(kPagedRowsPerWG * kHeadDim * 4);
+  auto slot_of = [&](int t) { return 2 * (3 * t + g) + (t == wa && t * run.per != fr ? 1 : 0); };
   float M = -INFINITY;
-  for (int j = 0; j < p.pieces; ++j) {
-    const uint32_t sb = (uint32_t)(group * p.pieces + j) * slot_bytes;
+  for (int wi = wa; wi <= wb; ++wi) {
+    const uint32_t sb = (uint32_t)slot_of(wi) * slot_bytes;
     M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0)));
   }
   f4 o[16];
 #pragma unroll
   for (int q = 0; q < 16; ++q) o[q] = f4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
-  for (int j = 0; j < p.pieces; ++j) {
-    const uint32_t sb = (uint32_t)(group * p.pieces + j) * slot_bytes;
+  for (int wi = wa; wi <= wb; ++wi) {
+    const uint32_t sb = (uint32_t)slot_of(wi) * slot_bytes;
     const float mj = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0));
     const float lj =
         __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kPagedRowsPerWG + rl) * 4, 0, 0));
@@ -418,8 +561,6 @@ __global__ __launch_bounds__(256) void paged_merge(PagedParams p) {
     }
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
-  const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-  const uint32_t obase = (uint32_t)row * kRowBytes + 128 * dq;
 #pragma unroll
   for (int q = 0; q < 16; q += 2) {
     const h2 a0 = cvt2(o[q][0] * inv, o[q][1] * inv), a1 = cvt2(o[q][2] * inv, o[q][3] * inv);
@@ -461,18 +602,15 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   p.off_entries = L.entries;
   p.off_part = L.part;
   p.part_bytes = (uint32_t)(L.total - L.part);
-  p.pieces = L.pieces;
   p.c = scale * kLog2e;
   hipLaunchKernelGGL(paged_prepass, dim3(p.nqb), dim3(kPrepassThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // ids are grouped by XCD (see paged_unit): round the query blocks up to a multiple of 8
-  const int units = ((p.nqb + 7) / 8) * 8 * kPagedWGsPerQBlock * p.pieces;
   prof_before(stream);
-  hipLaunchKernelGGL(paged_fwd, dim3(units), dim3(64 * kWaves), 0, stream, p);
+  hipLaunchKernelGGL(paged_fwd, dim3(kPagedGrid), dim3(64 * kWaves), 0, stream, p);
   e = hipGetLastError();
   prof_after(stream);
-  if (e != hipSuccess || p.pieces == 1) return e;
+  if (e != hipSuccess) return e;
   hipLaunchKernelGGL(paged_merge, dim3(p.nqb * kPagedWGsPerQBlock * 2), dim3(256), 0, stream, p);
   return hipGetLastError();
 }

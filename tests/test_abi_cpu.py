@@ -139,40 +139,36 @@ def _paged(**kw):
     (dict(n_table=1 << 20, page_size=4096, n_pages=1), g.GQA_ERR_UNSUPPORTED),
     (dict(n_table=(1 << 31) // 4096, page_size=4096, n_pages=1), g.GQA_ERR_UNSUPPORTED),  # exactly 2^31 tokens
     (dict(n_table=(1 << 31) // 4096 - 1, page_size=4096, n_pages=1), g.GQA_ERR_WORKSPACE),  # just below: accepted
-    # partials past the 32-bit workspace range (200000 rows, 512 ids per query block: 4 pieces)
-    (dict(nq=200000, n_ids=3125 * 512, q_pos0=0, live_len=200000, n_table=12500), g.GQA_ERR_UNSUPPORTED),
+    # a workspace past the 32-bit range (ids, then the fixed partial slots)
+    (dict(n_ids=525_000_000), g.GQA_ERR_UNSUPPORTED),
 ])
 def test_paged_rejects_before_launch(kw, status):
     assert _paged(**kw) == status
 
 
 @pytest.mark.parametrize("nq,n_ids", [(4096, 1000), (4096, 64 * 128), (4096, 64 * 512), (4096, 64 * 32),
-                                       (128, 6048), (64, 1)])
+                                       (128, 6048), (64, 1), (200000, 3125 * 512)])
 def test_paged_workspace_follows_the_layout(nq, n_ids):
     """Restated: a 16-byte header, three int32 per 64-token query block (rounded up to 16 bytes), 8 bytes
-    per id (rounded up to 256 bytes), then, when the average selection is longer than 32 blocks (2 pieces;
-    4 above 128), one fp32 partial of 128 rows (132096 bytes) per row group of 128 packed rows and piece."""
+    per id (rounded up to 256 bytes), then the partial slots: two per workgroup of the 168 teams of three
+    that share the work, one fp32 partial of 128 rows (132096 bytes) each."""
     nqb = -(-nq // 64)
     entries = -(-(16 + 12 * nqb) // 16) * 16
     part = -(-(entries + 8 * max(n_ids, 1)) // 256) * 256
-    avg = n_ids // nqb
-    pieces = 1 if avg <= 32 else 2 if avg <= 128 else 4
-    slots = nqb * 3 * pieces if pieces > 1 else 0
     n = ctypes.c_size_t()
     assert g.lib().gqa_prefill_paged_sparse_workspace_size(nq, n_ids, 64, 4, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
-    assert n.value == part + slots * (128 * 256 + 2 * 128) * 4
+    assert n.value == part + 1008 * (128 * 256 + 2 * 128) * 4
 
 
 def test_paged_workspace_stops_at_the_32_bit_range():
-    """The partial slots are addressed with 32-bit byte offsets: a layout past 2^32 - 1 bytes is refused."""
+    """The workspace is addressed with 32-bit byte offsets: a layout past 2^32 - 1 bytes is refused."""
     n = ctypes.c_size_t()
-    # 200000 rows = 3125 query blocks, 512 ids each: 4 pieces, 37500 slots of 132096 bytes (4.95 GB)
-    assert g.lib().gqa_prefill_paged_sparse_workspace_size(200000, 3125 * 512, 64, 4, 6, 1, 256,
+    # 525,000,000 ids (4.2 GB) fit the id check, but the partial slots behind them do not
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(4096, 525_000_000, 64, 4, 6, 1, 256,
                                                            ctypes.byref(n)) == g.GQA_ERR_UNSUPPORTED
-    # 100000 rows: 1563 query blocks, 18756 slots (2.48 GB) still fit
-    assert g.lib().gqa_prefill_paged_sparse_workspace_size(100000, 1563 * 512, 64, 4, 6, 1, 256,
+    assert g.lib().gqa_prefill_paged_sparse_workspace_size(4096, 500_000_000, 64, 4, 6, 1, 256,
                                                            ctypes.byref(n)) == g.GQA_OK
-    assert 2.4e9 < n.value < 2 ** 32
+    assert 4.0e9 < n.value < 2 ** 32
 
 
 def test_paged_workspace_query():
