@@ -26,15 +26,23 @@ constexpr int kQBlockRows = kQBlockTokens * 6;  // 384 packed rows
 constexpr int kPagedRowsPerWG = 128;
 constexpr int kPagedWGsPerQBlock = kQBlockRows / kPagedRowsPerWG;  // 3
 constexpr int kPagedMagic = 0x47514150;  // "PAQG"
-constexpr int kSortMax = 2048;           // selections up to this many blocks are sorted
+constexpr int kBitmapBlocks = 262144;    // tables of up to this many blocks (1M tokens) use the bitmap prepass
+constexpr int kDedupMax = 2048;          // beyond that, selections up to this many blocks are checked for repeats
 
 // The attention kernel cuts the work, sub-tiles of 32 keys of every query
-// block, into equal runs, each taken by a team of three workgroups (one per
-// 128-row group of the query block), 21 teams per XCD: 504 workgroups, two
-// per compute unit.  A team writes the query blocks it covers whole straight
-// to O; each of the two at its ends that it covers only in part leaves, per
-// row group, a partial of 128 rows (fp32 acc, m, l) in one of the workgroup's
-// two slots, which a merge kernel combines.
+// block, into runs of equal cost, each taken by a team of three workgroups
+// (one per 128-row group of the query block), 21 teams per XCD: 504
+// workgroups, two per compute unit.  A query block with n sub-tiles costs
+// n + kPagedSwitchUnits: starting on a query block (its Q rows, its first
+// gather, writing its result) takes about as long as that many sub-tiles.  A
+// team writes the query blocks it covers whole straight to O; each of the two
+// at its ends that it covers only in part leaves, per row group, a partial of
+// 128 rows (fp32 acc, m, l) in one of the workgroup's two slots, which a
+// merge kernel combines.
+constexpr int kPagedSwitchUnits = 3;
+// A run boundary that would leave fewer than this many sub-tiles of a query
+// block on one side moves to that block's start or end instead.
+constexpr int kPagedMinPiece = 2;
 constexpr int kPagedTeams = 168;  // 8 XCDs x 21 teams
 constexpr int kPagedGrid = 512;   // workgroup ids: 64 per XCD, 63 of them in teams
 constexpr int kPagedSlots = 2 * 3 * kPagedTeams;

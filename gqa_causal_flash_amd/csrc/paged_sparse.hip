@@ -57,12 +57,43 @@ struct PagedParams {
 };
 
 // ------------------------------------------------------------------ prepass
+constexpr int kHashSlots = 2 * kDedupMax;        // open-addressing table, at most half full
+constexpr int kBitmapWords = kBitmapBlocks / 32;  // one bit per logical block of the table
+constexpr int kPrepassWaves = kPrepassThreads / 64;
+
+// Exclusive prefix sum of v over the workgroup, and the total.  `wave_tot`
+// holds kPrepassWaves ints of LDS.
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_tot, int& total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < 64; d <<= 1) {
+    const int y = __shfl_up(incl, d);
+    if (lane >= d) incl += y;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  int before = 0;
+  total = 0;
+#pragma unroll
+  for (int w = 0; w < kPrepassWaves; ++w) {
+    const int t = wave_tot[w];
+    before += w < wave ? t : 0;
+    total += t;
+  }
+  return before + incl - v;
+}
+
 __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) {
-  __shared__ unsigned long long keys[kSortMax];
-  __shared__ unsigned long long keys2[kSortMax];
+  // the bitmap path uses bits + word prefixes, the hash path key + lowest index
+  __shared__ int lds_a[kBitmapWords];
+  __shared__ int lds_b[kBitmapWords];
+  static_assert(kHashSlots <= kBitmapWords, "the hash table fits the bitmap arrays");
+  __shared__ int small[kDedupMax / 64];
   __shared__ int errs;
   const int b = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
   const rsrc_t roff = make_rsrc(p.offsets, (uint32_t)(p.nqb + 1) * 4);
   const rsrc_t rids = make_rsrc(p.ids, (uint32_t)p.n_ids * 4);
   const rsrc_t rpt = make_rsrc(p.page_table, (uint32_t)p.n_table * 4);
@@ -79,7 +110,6 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     hdr[2] = p.n_ids;
     hdr[3] = 0;
   }
-  __syncthreads();
   const int o0 = (int)__builtin_amdgcn_raw_buffer_load_b32(roff, b * 4, 0, 0);
   const int o1 = (int)__builtin_amdgcn_raw_buffer_load_b32(roff, (b + 1) * 4, 0, 0);
   int start = min(max(o0, 0), p.n_ids);
@@ -90,139 +120,191 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
   const int blocks_per_page = p.page_size / kBlockTokens;
   const int n_blocks_table = p.n_table * blocks_per_page;
 
-  // Translate entry i of this block: valid -> (physical row << 32 | token),
-  // otherwise all ones (sorts last).
-  auto translate = [&](int i, int& bad) -> unsigned long long {
-    const int x = (int)__builtin_amdgcn_raw_buffer_load_b32(rids, (uint32_t)(start + i) * 4, 0, 0);
+  // Entry i of this block: valid -> {physical row of its first token, first
+  // token}; an id outside the table or a page outside the pool is an error; a
+  // block at or past the live length holds nothing and is dropped silently.
+  constexpr uint32_t kPastEnd = 0xFFFFFFF0u;  // a buffer offset that reads as 0
+  auto load_id = [&](int i) {
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rids, i < n ? (uint32_t)(start + i) * 4 : kPastEnd, 0, 0);
+  };
+  auto load_page = [&](int i, int x) {
+    const bool in_table = i < n && x >= 0 && x < n_blocks_table;
+    return (int)__builtin_amdgcn_raw_buffer_load_b32(rpt, in_table ? (uint32_t)(x / blocks_per_page) * 4 : kPastEnd,
+                                                     0, 0);
+  };
+  auto translate = [&](int i, int x, int page, int& bad) -> int2 {
+    if (i >= n) return int2{-1, 0};
     if (x < 0 || x >= n_blocks_table) {
-      bad = 1;
-      return ~0ull;
+      bad += 1;
+      return int2{-1, 0};
     }
     const int tok0 = x * kBlockTokens;
-    if (tok0 >= p.live_len) return ~0ull;  // stale block: not an error, just nothing live
-    const int page = (int)__builtin_amdgcn_raw_buffer_load_b32(rpt, (uint32_t)(x / blocks_per_page) * 4, 0, 0);
+    if (tok0 >= p.live_len) return int2{-1, 0};
     if (page < 0 || page >= p.n_pages) {
-      bad = 1;
-      return ~0ull;
+      bad += 1;
+      return int2{-1, 0};
     }
-    const unsigned row = (unsigned)page * (unsigned)p.page_size + (unsigned)(x % blocks_per_page) * kBlockTokens;
-    return ((unsigned long long)row << 32) | (unsigned)tok0;
+    return int2{page * p.page_size + (x % blocks_per_page) * kBlockTokens, tok0};
+  };
+  // Selections of up to kDedupMax entries are held in registers (thread t:
+  // entries t + 512 r), with the R id loads, then the R page-table loads, in
+  // flight together.
+  constexpr int R = kDedupMax / kPrepassThreads;
+  int xs[R];
+  int2 e[R];
+  int bad = 0, dups = 0;
+  auto load_all = [&]() {
+    int pages[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) xs[r] = load_id(tid + kPrepassThreads * r);
+#pragma unroll
+    for (int r = 0; r < R; ++r) pages[r] = load_page(tid + kPrepassThreads * r, xs[r]);
+#pragma unroll
+    for (int r = 0; r < R; ++r) e[r] = translate(tid + kPrepassThreads * r, xs[r], pages[r], bad);
   };
 
-  if (n <= kSortMax) {
-    int npow = 1;
-    while (npow < n) npow <<= 1;
-    int bad = 0;
-    // Bitonic sort, ascending, with the keys in registers: thread t holds
-    // elements t + 512 r (r < kSortMax / 512).  A compare-exchange at distance
-    // j pairs lanes of one wave when j < 64 (register shuffle, no barrier), a
-    // thread with itself when j >= 512, and otherwise goes through LDS (two
-    // buffers, one barrier per such stage).
-    constexpr int R = kSortMax / kPrepassThreads;
-    unsigned long long kv[R];
+  if (n_blocks_table <= kBitmapBlocks) {
+    // The selection is a set of logical blocks: one bit per block of the
+    // table.  A repeated id finds its bit set and is counted; the kept blocks
+    // are packed in logical order (block x goes to the number of set bits
+    // below x), which keeps the blocks of a page together.  Any length.
+    unsigned* bits = (unsigned*)lds_a;
+    int* word_before = lds_b;
+    const int words = (n_blocks_table + 31) >> 5;
+    for (int w = tid; w < words; w += kPrepassThreads) bits[w] = 0u;
+    if (n <= kDedupMax) load_all();
+    __syncthreads();  // the bitmap is clear
+    auto mark = [&](int x, int2 en) {
+      if (en.x < 0) return;
+      const unsigned bit = 1u << (x & 31);
+      if (atomicOr(&bits[x >> 5], bit) & bit) ++dups;
+    };
+    if (n <= kDedupMax) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) mark(xs[r], e[r]);
+    } else {
+      for (int i = tid; i < n; i += kPrepassThreads) {
+        const int x = load_id(i);
+        mark(x, translate(i, x, load_page(i, x), bad));
+      }
+    }
+    __syncthreads();
+    // set bits before each word: thread t counts words t*wpt .. t*wpt+wpt-1
+    const int wpt = (words + kPrepassThreads - 1) / kPrepassThreads;
+    int c = 0;
+    for (int k = 0; k < wpt; ++k) {
+      const int w = tid * wpt + k;
+      c += w < words ? __popc(bits[w]) : 0;
+    }
+    int total;
+    int run = block_exclusive_scan(c, small, total);
+    for (int k = 0; k < wpt; ++k) {
+      const int w = tid * wpt + k;
+      if (w < words) {
+        word_before[w] = run;
+        run += __popc(bits[w]);
+      }
+    }
+    __syncthreads();
+    // every copy of a block writes the same entry to the same place
+    auto place = [&](int x, int2 en) {
+      if (en.x < 0) return;
+      const int at = word_before[x >> 5] + __popc(bits[x >> 5] & ((1u << (x & 31)) - 1u));
+      ent[start + at] = en;
+    };
+    if (n <= kDedupMax) {
+#pragma unroll
+      for (int r = 0; r < R; ++r) place(xs[r], e[r]);
+    } else {
+      int bad2 = 0;  // counted in the first pass
+      for (int i = tid; i < n; i += kPrepassThreads) {
+        const int x = load_id(i);
+        place(x, translate(i, x, load_page(i, x), bad2));
+      }
+    }
+    if (bad + dups) atomicAdd(&errs, bad + dups);
+    if (tid == 0) {
+      cnt[b] = total;
+      beg[b] = start;
+    }
+  } else if (n <= kDedupMax) {
+    // A table too large for the bitmap: repeats are found through an
+    // open-addressing table (the copy with the lowest index stays), and the
+    // kept entries are packed in the given order.
+    int* hkey = lds_a;  // block id held by a slot, -1: empty
+    int* hmin = lds_b;  // lowest entry index holding that id
+    for (int sl = tid; sl < kHashSlots; sl += kPrepassThreads) {
+      hkey[sl] = -1;
+      hmin[sl] = 0x7FFFFFFF;
+    }
+    load_all();
+    __syncthreads();  // the table is clear
+    int hslot[R];
 #pragma unroll
     for (int r = 0; r < R; ++r) {
-      const int i = tid + kPrepassThreads * r;
-      kv[r] = (i < n) ? translate(i, bad) : ~0ull;
-    }
-    if (bad) atomicAdd(&errs, bad);
-    const int rmax = (npow + kPrepassThreads - 1) / kPrepassThreads;  // register slots in use
-    // The stages are written for a compile-time count of slots in use, so
-    // that a stage issues the exchanges of all its slots before it waits.
-    auto sort_slots = [&](auto rmc) {
-      constexpr int RM = decltype(rmc)::value;
-      int buf = 0;
-      for (int k = 2; k <= npow; k <<= 1) {
-        for (int j = k >> 1; j > 0; j >>= 1) {
-          if (j >= kPrepassThreads) {
-            const int rj = j / kPrepassThreads;
-#pragma unroll
-            for (int r = 0; r < RM; ++r) {
-              const int rp = r ^ rj;
-              const int i = tid + kPrepassThreads * r;
-              if (rp > r && rp < RM) {
-                const bool up = (i & k) == 0;
-                const unsigned long long a = kv[r], c = kv[rp];
-                if ((a > c) == up) {
-                  kv[r] = c;
-                  kv[rp] = a;
-                }
-              }
-            }
-          } else {
-            unsigned long long c[RM];
-            if (j < 64) {
-#pragma unroll
-              for (int r = 0; r < RM; ++r) c[r] = __shfl_xor(kv[r], j);
-            } else {
-              unsigned long long* kb = buf ? keys2 : keys;
-#pragma unroll
-              for (int r = 0; r < RM; ++r) kb[tid + kPrepassThreads * r] = kv[r];
-              __syncthreads();
-#pragma unroll
-              for (int r = 0; r < RM; ++r) c[r] = kb[(tid + kPrepassThreads * r) ^ j];
-              buf ^= 1;
-            }
-#pragma unroll
-            for (int r = 0; r < RM; ++r) {
-              const int i = tid + kPrepassThreads * r;
-              const unsigned long long a = kv[r];
-              const bool up = (i & k) == 0;
-              const bool lo = (i & j) == 0;  // the lower index of the pair keeps the smaller key when ascending
-              kv[r] = (lo == up) ? (a < c[r] ? a : c[r]) : (a < c[r] ? c[r] : a);
-            }
-          }
-        }
+      hslot[r] = -1;
+      if (e[r].x < 0) continue;
+      uint32_t sl = ((uint32_t)xs[r] * 2654435761u) >> (32 - 12);  // Fibonacci hashing into 4096 slots
+      static_assert(kHashSlots == 4096, "12-bit hash");
+      for (;;) {
+        const int prev = atomicCAS(&hkey[sl], -1, xs[r]);
+        if (prev == -1 || prev == xs[r]) break;
+        sl = (sl + 1) & (kHashSlots - 1);
       }
-    };
-    static_assert(R == 4, "slot counts 1, 2 and 4");
-    if (rmax <= 1)
-      sort_slots(std::integral_constant<int, 1>{});
-    else if (rmax == 2)
-      sort_slots(std::integral_constant<int, 2>{});
-    else
-      sort_slots(std::integral_constant<int, 4>{});
+      atomicMin(&hmin[sl], tid + kPrepassThreads * r);
+      hslot[r] = (int)sl;
+    }
+    __syncthreads();
+    bool keep[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      keep[r] = hslot[r] >= 0 && hmin[hslot[r]] == tid + kPrepassThreads * r;
+      dups += (hslot[r] >= 0 && !keep[r]) ? 1 : 0;
+    }
+    // stable compaction: entry i's place is the number of kept entries before
+    // it; entries are numbered r-major (t + 512 r), so the count runs over the
+    // (r, wave) groups in order, then over the lanes below inside the group
+    unsigned long long bal[R];
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      bal[r] = __ballot(keep[r]);
+      if (lane == 0) small[r * kPrepassWaves + wave] = __popcll(bal[r]);
+    }
+    __syncthreads();
+    int before_group[R];
+    int total = 0;
+    for (int gi = 0; gi < R * kPrepassWaves; ++gi) {
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+        if (gi == r * kPrepassWaves + wave) before_group[r] = total;
+      total += small[gi];
+    }
+    const unsigned long long below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
 #pragma unroll
     for (int r = 0; r < R; ++r)
-      if (r < rmax) keys[tid + kPrepassThreads * r] = kv[r];
-    __syncthreads();
-    // drop duplicates (same physical row) and count the valid prefix
-    int dup = 0, valid = 0;
-    for (int i = tid; i < n; i += kPrepassThreads) {
-      unsigned long long kv = keys[i];
-      if (kv != ~0ull && i > 0 && (keys[i - 1] >> 32) == (kv >> 32)) {
-        kv = ~0ull;
-        dup = 1;
-      }
-      if (kv != ~0ull) valid = i + 1;
-      ent[start + i] = (kv == ~0ull) ? int2{-1, 0x7FFFFFFF} : int2{(int)(kv >> 32), (int)(kv & 0xFFFFFFFFu)};
-    }
-    if (dup) atomicAdd(&errs, 1);
-    __shared__ int vmax;
-    if (tid == 0) vmax = 0;
-    __syncthreads();
-    if (valid) atomicMax(&vmax, valid);
-    __syncthreads();
+      if (keep[r]) ent[start + before_group[r] + __popcll(bal[r] & below)] = e[r];
+    if (bad + dups) atomicAdd(&errs, bad + dups);
     if (tid == 0) {
-      cnt[b] = vmax;
+      cnt[b] = total;
       beg[b] = start;
-      err[b] = errs + bad_range;
     }
   } else {
-    // too long to sort in LDS: keep the given order (it is only a locality choice)
-    int bad = 0;
+    // a long selection over a table too large for the bitmap: the given order,
+    // with an entry that holds nothing live kept in place as {-1, INT32_MAX};
+    // a repeated id is not detected
     for (int i = tid; i < n; i += kPrepassThreads) {
-      const unsigned long long kv = translate(i, bad);
-      ent[start + i] = (kv == ~0ull) ? int2{-1, 0x7FFFFFFF} : int2{(int)(kv >> 32), (int)(kv & 0xFFFFFFFFu)};
+      const int x = load_id(i);
+      const int2 t = translate(i, x, load_page(i, x), bad);
+      ent[start + i] = t.x < 0 ? int2{-1, 0x7FFFFFFF} : t;
     }
     if (bad) atomicAdd(&errs, bad);
-    __syncthreads();
     if (tid == 0) {
       cnt[b] = n;
       beg[b] = start;
-      err[b] = errs + bad_range;
     }
   }
+  __syncthreads();  // errs complete
+  if (tid == 0) err[b] = errs + bad_range;
 }
 
 // ------------------------------------------------------------------ attention
@@ -233,66 +315,135 @@ constexpr int kDeadToken = 0x7FFFFFFF;           // token of an entry that holds
 // sees: its own wait insertion then knows that every load has landed
 constexpr int kWaitVmcnt0 = 0x0F70;
 
-// Work units.  Query block b needs n_b = ceil(cnt[b] / 8) sub-tiles of 32
-// keys for each of its three row groups.  Column unit (b, x) is sub-tile x of
-// query block b, numbered query block by query block; the C column units are
-// cut into equal runs of `per` consecutive units, and each run goes to a team
-// of three workgroups, one per row group, which stream the same sub-tiles at
-// the same pace: the team runs on one XCD, so two of the three gathers of
-// every block come from that XCD's L2.  Every compute unit gets the same work
-// whatever the selection lengths.  A run covers the tail of one query block,
-// whole query blocks and the head of another: whole ones are written straight
-// to O, and the (at most two) cut ones leave a partial of the row group in the
+// Work positions.  Query block b needs n_b = ceil(cnt[b] / 8) sub-tiles of 32
+// keys for each of its three row groups.  A query block with n_b > 0 takes
+// w_b = kPagedSwitchUnits + n_b consecutive positions, numbered query block by
+// query block from F_b = w_0 + ... + w_(b-1): the first kPagedSwitchUnits
+// stand for the cost of starting on it, then sub-tile x sits at position
+// base_b + x, base_b = F_b + kPagedSwitchUnits.  The positions are cut into
+// equal runs of `per`, and each run goes to a team of three workgroups, one
+// per row group, which stream the same sub-tiles at the same pace: the team
+// runs on one XCD, so two of the three gathers of every block come from that
+// XCD's L2.  Every compute unit gets about the same work whatever the
+// selection lengths.  A boundary t * per that would cut fewer than
+// kPagedMinPiece sub-tiles off a query block moves to that block's start or
+// end (PagedSched::bound), so small query blocks stay whole.  A run covers the tail
+// of one query block, whole query blocks and the head of another: whole ones
+// are written straight to O, and
+// the (at most two) cut ones leave a partial of the row group in the
 // workgroup's slots 2w (its first query block) and 2w + 1 (its last), with
 // w = 3 team + g, which paged_merge combines.
 __device__ __forceinline__ int paged_nsub(const int* cnt, int b) { return (cnt[b] + 7) >> 3; }
+__device__ __forceinline__ int paged_weight(const int* cnt, int b) {
+  const int n = paged_nsub(cnt, b);
+  return n > 0 ? n + kPagedSwitchUnits : 0;
+}
 
 struct PagedRun {
-  int per;     // column units per team
-  int total;   // all column units
-  int teams;   // teams with work
+  int per;    // positions per team
+  int total;  // all positions
+  int teams;  // teams with work
 };
 
-// Sum over query blocks, computed by each wave on its own (64 query blocks per step).
-__device__ __forceinline__ PagedRun paged_run(const int* cnt, int nqb, int lane) {
-  int t = 0;
-  for (int b0 = 0; b0 < nqb; b0 += 64) {
-    const int b = b0 + lane;
-    t += b < nqb ? paged_nsub(cnt, b) : 0;
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
-  PagedRun r;
-  r.total = __builtin_amdgcn_readfirstlane(t);
-  r.per = max((r.total + kPagedTeams - 1) / kPagedTeams, 2);
-  r.teams = (r.total + r.per - 1) / r.per;
-  return r;
-}
+// The schedule as one wave sees it.  The weights of query blocks 0..63 are
+// read once, one per lane, with their inclusive prefix; later query blocks
+// (when there are more than 64) are read as needed, 64 per step.  Every
+// result is wave-uniform.
+struct PagedSched {
+  const int* cnt;
+  int nqb, lane;
+  int w0, incl0, tot0;  // lane's weight and inclusive prefix in blocks 0..63; their sum
+  PagedRun run;
 
-// The query block holding column unit u and its first unit (u < total).
-__device__ __forceinline__ void paged_find(const int* cnt, int nqb, int lane, int u, int& qb, int& first) {
-  int base = 0;
-  for (int b0 = 0; b0 < nqb; b0 += 64) {
-    const int b = b0 + lane;
-    const int n = b < nqb ? paged_nsub(cnt, b) : 0;
-    int incl = n;  // inclusive prefix over the 64 lanes
+  __device__ __forceinline__ PagedSched(const int* c, int n, int ln) : cnt(c), nqb(n), lane(ln) {
+    w0 = lane < nqb ? paged_weight(cnt, lane) : 0;
+    incl0 = w0;
 #pragma unroll
     for (int d = 1; d < 64; d <<= 1) {
-      const int y = __shfl_up(incl, d);
-      if (lane >= d) incl += y;
+      const int y = __shfl_up(incl0, d);
+      if (lane >= d) incl0 += y;
     }
-    const unsigned long long hit = __ballot(base + incl > u);
-    if (hit) {
+    tot0 = __builtin_amdgcn_readlane(incl0, 63);
+    int t = 0;
+    for (int b0 = 64; b0 < nqb; b0 += 64) {
+      const int b = b0 + lane;
+      t += b < nqb ? paged_weight(cnt, b) : 0;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
+    run.total = tot0 + __builtin_amdgcn_readfirstlane(t);
+    run.per = max((run.total + kPagedTeams - 1) / kPagedTeams, 2);
+    run.teams = (run.total + run.per - 1) / run.per;
+  }
+
+  // sub-tiles of query block b
+  __device__ __forceinline__ int nsub(int b) const {
+    if (b < 64) {
+      const int w = __builtin_amdgcn_readlane(w0, b);
+      return w > 0 ? w - kPagedSwitchUnits : 0;
+    }
+    return __builtin_amdgcn_readfirstlane(paged_nsub(cnt, b));
+  }
+
+  // F_b: the positions of the query blocks before b
+  __device__ __forceinline__ int first_of(int b) const {
+    if (b < 64) return b == 0 ? 0 : __builtin_amdgcn_readlane(incl0, b - 1);
+    int t = 0;
+    for (int b0 = 64; b0 < b; b0 += 64) {
+      const int bb = b0 + lane;
+      t += bb < b ? paged_weight(cnt, bb) : 0;
+    }
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
+    return tot0 + __builtin_amdgcn_readfirstlane(t);
+  }
+
+  // The first query block whose positions reach past position u (u < total),
+  // and its first position F_b; it always has sub-tiles.
+  __device__ __forceinline__ void find(int u, int& qb, int& first) const {
+    if (u < tot0) {
+      const unsigned long long hit = __ballot(incl0 > u);
       const int l = __builtin_ctzll(hit);
-      qb = b0 + l;
-      first = __builtin_amdgcn_readfirstlane(base + __shfl(incl - n, l));
+      qb = l;
+      first = l == 0 ? 0 : __builtin_amdgcn_readlane(incl0, l - 1);
       return;
     }
-    base = __builtin_amdgcn_readfirstlane(base + __shfl(incl, 63));
+    int base = tot0;
+    for (int b0 = 64; b0 < nqb; b0 += 64) {
+      const int b = b0 + lane;
+      const int n = b < nqb ? paged_weight(cnt, b) : 0;
+      int incl = n;  // inclusive prefix over the 64 lanes
+#pragma unroll
+      for (int d = 1; d < 64; d <<= 1) {
+        const int y = __shfl_up(incl, d);
+        if (lane >= d) incl += y;
+      }
+      const unsigned long long hit = __ballot(base + incl > u);
+      if (hit) {
+        const int l = __builtin_ctzll(hit);
+        qb = b0 + l;
+        first = base + (l == 0 ? 0 : __builtin_amdgcn_readlane(incl, l - 1));
+        return;
+      }
+      base += __builtin_amdgcn_readlane(incl, 63);
+    }
+    qb = nqb;
+    first = base;
   }
-  qb = nqb;
-  first = base;
-}
+
+  // First position of team t's run (t <= teams; the end of the last run is total).
+  __device__ __forceinline__ int bound(int t) const {
+    const int u = t * run.per;
+    if (u >= run.total) return run.total;
+    int b, first;
+    find(u, b, first);
+    const int n = nsub(b);
+    const int before = max(0, u - first - kPagedSwitchUnits);  // sub-tiles of b before u
+    if (before < kPagedMinPiece) return first;
+    if (n - before < kPagedMinPiece) return first + kPagedSwitchUnits + n;
+    return u;
+  }
+};
 
 // Wave w stages rows 8w .. 8w+7 of a 32-key sub-tile, i.e. entries 2w, 2w+1
 // of the sub-tile; copy i covers rows 8w+2i, 8w+2i+1 = tokens 2(i%2), 2(i%2)+1
@@ -376,7 +527,8 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   const int* cnt = (const int*)(p.ws + p.off_cnt);
   const int* begp = (const int*)(p.ws + p.off_beg);
   const int2* ent = (const int2*)(p.ws + p.off_entries);
-  const PagedRun run = paged_run(cnt, p.nqb, lane);
+  const PagedSched sched(cnt, p.nqb, lane);
+  const PagedRun& run = sched.run;
   // Workgroup ids are dealt to the 8 XCDs in turn; an XCD's 64 ids hold 21
   // teams of three.  The teams with work are cut into 8 contiguous groups, one
   // per XCD, so that every XCD gets an equal share however few teams there are.
@@ -386,11 +538,11 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   const int team = (blockIdx.x & 7) * per_xcd + xi / 3;
   const int g = xi % 3;  // this workgroup's row group
   const int w = 3 * team + g;
-  int u = team * run.per;
-  const int u_end = min(run.total, u + run.per);
-  if (u >= u_end) return;
+  const int u0 = sched.bound(team);  // the team's positions u0 .. u_end-1
+  const int u_end = sched.bound(team + 1);
+  if (u0 >= u_end) return;
   int b, first;
-  paged_find(cnt, p.nqb, lane, u, b, first);
+  sched.find(u0, b, first);
 
   const rsrc_t rq = make_rsrc(p.q, (uint32_t)p.nrows * kRowBytes);
   const uint32_t cache_bytes = (uint32_t)p.n_pages * (uint32_t)p.page_size * kRowBytes;
@@ -400,13 +552,15 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   uint32_t bv = v_lane_base(lane);
 
   bool first_seg = true;
-  while (u < u_end) {
+  while (b < p.nqb) {
     // the segment: sub-tiles s0 .. s1-1 of row group g of query block b (all
     // wave-uniform: kept in scalar registers)
     const int count = __builtin_amdgcn_readfirstlane(cnt[b]);
     const int nb = (count + 7) >> 3;
-    const int s0 = u - first;
-    const int s1 = min(nb, s0 + (u_end - u));
+    const int base = first + kPagedSwitchUnits;  // position of sub-tile 0
+    const int s0 = max(0, u0 - base);
+    const int s1 = min(nb, u_end - base);
+    if (s1 <= s0) break;  // the run ends before this block's first sub-tile
     const int e_beg = __builtin_amdgcn_readfirstlane(begp[b]);
     const int e_end = e_beg + count;
 
@@ -488,81 +642,109 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
                     m[0], lt);
     }
     first_seg = false;
-    u += s1 - s0;
-    if (u >= u_end) break;
-    // next query block; those with nothing selected hold no units
-    first += nb;
+    if (base + s1 >= u_end) break;
+    // next query block; those with nothing selected hold no positions
+    first = base + nb;
     ++b;
     while (b < p.nqb && __builtin_amdgcn_readfirstlane(cnt[b]) == 0) ++b;
   }
 }
 
-// Merge of the cut row groups: workgroup (row group, half) takes 64 rows;
-// thread (row, 64 columns).  Query block b holds column units first_b ..
-// first_b + n_b - 1; the teams t_a = first_b / per .. t_b = (first_b + n_b - 1)
-// / per cover it.  One team means its row groups were written whole;
-// otherwise the row-group-g workgroup of team t_a contributes slot 2w (if b is
-// its first query block) or 2w + 1, and that of every later team slot 2w
-// (w = 3 team + g).  A query block with nothing selected is written as zeros.
+// Merge of the cut row groups.  Workgroup (query block b, row group g, row
+// half, column half) takes 64 rows x 128 columns; thread (row, 32 columns).
+// The sub-tiles of query block b sit at positions base_b .. base_b + n_b - 1;
+// the teams t_a .. t_b whose runs hold the first and the last of them cover
+// it.  One team means its row groups were written whole; otherwise the
+// row-group-g workgroup of team t_a contributes slot 2w + 1 if the sub-tiles
+// of an earlier query block fall in its run (the last of them sits at
+// F_b - 1), else slot 2w, and that of every later team slot 2w
+// (w = 3 team + g).  The
+// pieces are combined in one pass with a running maximum (the log-sum-exp
+// merge), and the next piece's loads are in flight while one is combined.  A
+// query block with nothing selected is written as zeros.
+constexpr int kMergeWGsPerRowGroup = 4;  // 2 row halves x 2 column halves
+
 __global__ __launch_bounds__(256) void paged_merge(PagedParams p) {
-  const int group = blockIdx.x >> 1;  // = b * 3 + g
+  const int group = blockIdx.x / kMergeWGsPerRowGroup;  // = b * 3 + g
+  const int sub = blockIdx.x % kMergeWGsPerRowGroup;
   const int b = group / kPagedWGsPerQBlock, g = group % kPagedWGsPerQBlock;
-  const int rl = (blockIdx.x & 1) * 64 + (threadIdx.x & 63);
-  const int dq = threadIdx.x >> 6;
   const int lane = threadIdx.x & 63;
+  const int rl = (sub & 1) * 64 + lane;                      // row inside the row group
+  const int c0 = (sub >> 1) * 128 + 32 * (threadIdx.x >> 6);  // first of the thread's 32 columns
   const int row = group * kPagedRowsPerWG + rl;
   const int* cnt = (const int*)(p.ws + p.off_cnt);
-  const PagedRun run = paged_run(cnt, p.nqb, lane);
-  // first column unit of query block b: the sum over the blocks before it
-  int before = 0;
-  for (int b0 = 0; b0 < b; b0 += 64) {
-    const int bb = b0 + lane;
-    before += bb < b ? paged_nsub(cnt, bb) : 0;
-  }
-#pragma unroll
-  for (int d = 32; d >= 1; d >>= 1) before += __shfl_xor(before, d);
+  // the schedule is worked out by the whole wave before any lane leaves
+  const PagedSched sched(cnt, p.nqb, lane);
+  const PagedRun& run = sched.run;
+  const int before = sched.first_of(b);  // F_b
+  const int nb = sched.nsub(b);
+  // the team whose run holds position q: a boundary moves by less than
+  // kPagedSwitchUnits + kPagedMinPiece, which bounds the search
+  int bound_found = 0;
+  auto team_of = [&](int q) {
+    int t = min(run.teams - 1, (q + kPagedSwitchUnits + kPagedMinPiece) / run.per);
+    int bt = sched.bound(t);
+    while (t > 0 && bt > q) bt = sched.bound(--t);
+    bound_found = bt;
+    return t;
+  };
+  const int fr = before + kPagedSwitchUnits;  // position of sub-tile 0
+  const int wb = nb > 0 ? team_of(fr + nb - 1) : 0;
+  const int wa = nb > 0 ? team_of(fr) : 0;  // its run starts at bound_found
+  const bool wa_has_earlier = bound_found < before;
   if (row >= min(p.nrows, (b + 1) * kQBlockRows)) return;
-  const int nb = paged_nsub(cnt, b);
   const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
-  const uint32_t obase = (uint32_t)row * kRowBytes + 128 * dq;
+  const uint32_t obase = (uint32_t)row * kRowBytes + 2 * c0;
   if (nb == 0) {
 #pragma unroll
-    for (int q = 0; q < 16; q += 2) store_16B(ro, obase + q * 8, u4{0u, 0u, 0u, 0u});
+    for (int q = 0; q < 4; ++q) store_16B(ro, obase + 16 * q, u4{0u, 0u, 0u, 0u});
     return;
   }
-  const int fr = before;
-  const int wa = fr / run.per, wb = (fr + nb - 1) / run.per;  // teams
   if (wa == wb) return;
   const rsrc_t rp = make_rsrc(p.ws + p.off_part, p.part_bytes);
   const uint32_t slot_bytes = (uint32_t)(kPagedSlotFloats * 4);
   const uint32_t m_off = (uint32_t)(kPagedRowsPerWG * kHeadDim * 4);
-  auto slot_of = [&](int t) { return 2 * (3 * t + g) + (t == wa && t * run.per != fr ? 1 : 0); };
-  float M = -INFINITY;
-  for (int wi = wa; wi <= wb; ++wi) {
-    const uint32_t sb = (uint32_t)slot_of(wi) * slot_bytes;
-    M = fmaxf(M, __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0)));
-  }
-  f4 o[16];
+  auto slot_of = [&](int t) { return 2 * (3 * t + g) + (t == wa && wa_has_earlier ? 1 : 0); };
+  struct Piece {
+    float m, l;
+    f4 x[8];
+  };
+  // the thread's column quads are c0/4 .. c0/4 + 7, each a run of 16-byte rows
+  auto load = [&](int t, Piece& pc) {
+    const uint32_t sb = (uint32_t)slot_of(t) * slot_bytes;
+    pc.m = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0));
+    pc.l = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kPagedRowsPerWG + rl) * 4, 0, 0));
 #pragma unroll
-  for (int q = 0; q < 16; ++q) o[q] = f4{0.f, 0.f, 0.f, 0.f};
-  float L = 0.f;
-  for (int wi = wa; wi <= wb; ++wi) {
-    const uint32_t sb = (uint32_t)slot_of(wi) * slot_bytes;
-    const float mj = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + rl * 4, 0, 0));
-    const float lj =
-        __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + m_off + (kPagedRowsPerWG + rl) * 4, 0, 0));
-    const float a = (mj == -INFINITY) ? 0.f : fast_exp2(mj - M);
-    L += a * lj;
+    for (int q = 0; q < 8; ++q)
+      pc.x[q] = __builtin_bit_cast(
+          f4, __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((c0 / 4 + q) * kPagedRowsPerWG + rl) * 16), 0, 0));
+  };
+  float M = -INFINITY, L = 0.f;
+  f4 o[8];
 #pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const u4 x =
-          __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((16 * dq + q) * kPagedRowsPerWG + rl) * 16), 0, 0);
-      o[q] += a * __builtin_bit_cast(f4, x);
-    }
+  for (int q = 0; q < 8; ++q) o[q] = f4{0.f, 0.f, 0.f, 0.f};
+  auto combine = [&](const Piece& pc) {
+    if (pc.m == -INFINITY) return;  // nothing visible in this piece
+    const float mn = fmaxf(M, pc.m);
+    const float a = (M == -INFINITY) ? 0.f : fast_exp2(M - mn);
+    const float e = fast_exp2(pc.m - mn);
+    L = a * L + e * pc.l;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = a * o[q] + e * pc.x[q];
+    M = mn;
+  };
+  Piece p0, p1;
+  load(wa, p0);
+  for (int t = wa; t <= wb; t += 2) {
+    if (t + 1 <= wb) load(t + 1, p1);
+    combine(p0);
+    if (t + 1 > wb) break;
+    if (t + 2 <= wb) load(t + 2, p0);
+    combine(p1);
   }
   const float inv = L > 0.f ? 1.0f / L : 0.f;
 #pragma unroll
-  for (int q = 0; q < 16; q += 2) {
+  for (int q = 0; q < 8; q += 2) {
     const h2 a0 = cvt2(o[q][0] * inv, o[q][1] * inv), a1 = cvt2(o[q][2] * inv, o[q][3] * inv);
     const h2 b0 = cvt2(o[q + 1][0] * inv, o[q + 1][1] * inv), b1 = cvt2(o[q + 1][2] * inv, o[q + 1][3] * inv);
     const h8 v = {a0[0], a0[1], a1[0], a1[1], b0[0], b0[1], b1[0], b1[1]};
@@ -611,7 +793,7 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   e = hipGetLastError();
   prof_after(stream);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(paged_merge, dim3(p.nqb * kPagedWGsPerQBlock * 2), dim3(256), 0, stream, p);
+  hipLaunchKernelGGL(paged_merge, dim3(p.nqb * kPagedWGsPerQBlock * kMergeWGsPerRowGroup), dim3(256), 0, stream, p);
   return hipGetLastError();
 }
 

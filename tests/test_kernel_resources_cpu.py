@@ -31,7 +31,7 @@ EXPECTED = {
     "prefill_merge": (0, 256, 0),
     "prefill_merge_varlen": (0, 256, 0),
     "prefill_varlen_prepass": (1024, 512, 0),
-    "paged_prepass": (32776, 512, 0),
+    "paged_prepass": (65668, 512, 0),
     "paged_fwd": (65792, 256, 0),                # 2 workgroups of 4 waves per CU
     "paged_merge": (0, 256, 0),
     "verify_fwd<1>": (81920, 512, 0),            # 2 workgroups of 2 waves per CU: 1 wave per SIMD

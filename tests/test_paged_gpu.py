@@ -46,6 +46,15 @@ def test_paged_parity_config(select, tail):
     assert_parity(_gpu(x), _oracle(x), f"S={select} t={tail}")
 
 
+def test_paged_short_last_query_block_of_64():
+    """4090 query tokens: 64 query blocks, the last one 58 tokens long, with selections long enough
+    that query blocks are split between teams; the merge workgroups of the last query block have
+    lanes past the last row."""
+    x = workloads.paged_sparse_inputs(select_tokens=2048, tail=2, seed=8, nq=4090)
+    assert x.qblock_offsets.size - 1 == 64
+    assert_parity(_gpu(x), _oracle(x), "nq=4090")
+
+
 def test_paged_128_entry_table():
     """The 128-entry page-16 table geometry: 2044 rows (short last query block)."""
     x = workloads.paged_sparse_inputs(select_tokens=512, tail=3, seed=7, nq=2044)
@@ -112,9 +121,9 @@ def test_paged_saturated_matches_dense_causal():
     assert_parity(out, ref, "saturated")
 
 
-def test_paged_selection_longer_than_the_sort_is_taken_in_order():
-    """More than 2048 blocks in one query block: the prepass keeps the given (shuffled) order instead
-    of sorting; 128 rows at positions 12000.., every earlier block selected (about 3000 per block)."""
+def test_paged_selection_longer_than_2048_blocks():
+    """About 3000 blocks in one query block (128 rows at positions 12000.., every earlier block
+    selected): the prepass's bitmap takes selections of any length."""
     x = workloads.paged_sparse_inputs(select_tokens=64, tail=12000, seed=41, nq=128, n_pages=1024, saturate=True)
     assert np.diff(x.qblock_offsets).min() > 2048
     assert_parity(_gpu(x), _oracle(x), "3000-block selections")
@@ -177,6 +186,49 @@ def test_paged_invalid_and_duplicate_entries_are_dropped():
     assert n_victim > 0
     assert dropped == 2 + n_victim
     assert_parity(out, ref, "dropped entries")
+
+
+def test_paged_repeated_ids_are_dropped_across_the_whole_check_range():
+    """Query blocks of 1800 distinct ids plus 200 repeats inserted at random places (drawn with
+    replacement, so some ids occur three times): 2000 entries, so every one of the thread's four
+    entry groups holds kept entries.  Each repeat is dropped and counted once, and the result equals
+    the oracle on the selection as a set."""
+    import gqa_causal_flash_amd as g
+
+    x = workloads.paged_sparse_inputs(select_tokens=4 * 1800, tail=8000, seed=42, nq=128, n_pages=1024)
+    rng = np.random.default_rng(43)
+    offs = x.qblock_offsets
+    ids, new_offs, n_rep = [], [0], 0
+    for b in range(len(offs) - 1):
+        sel = [int(i) for i in x.kv_block_ids[offs[b]:offs[b + 1]]]
+        assert len(set(sel)) == len(sel) == 1800
+        for r in rng.choice(sel, size=200, replace=True):
+            sel.insert(int(rng.integers(0, len(sel) + 1)), int(r))
+        n_rep += 200
+        assert 1536 < len(sel) <= 2048
+        ids += sel
+        new_offs.append(len(ids))
+    ids = np.asarray(ids, dtype=np.int32)
+    new_offs = np.asarray(new_offs, dtype=np.int32)
+    out, ws = _gpu(x, ids=ids, offs=new_offs, want_ws=True)
+    assert g.gqa_prefill_paged_sparse_dropped(ws) == n_rep
+    assert_parity(out, _oracle(x, ids=ids, offs=new_offs), "repeated ids")
+
+
+@pytest.mark.parametrize("n_select,n_repeat", [(1500, 100), (3000, 0)])
+def test_paged_table_beyond_the_bitmap(n_select, n_repeat):
+    """A request of 70000 pages of 16 tokens (1.12M tokens, past the prepass bitmap's 262144
+    blocks) held in a 64-page pool, selections spread over the whole table: 1500 ids plus 100
+    repeats take the open-addressing path (each repeat dropped and counted), 3000 distinct ids the
+    long path (given order)."""
+    import gqa_causal_flash_amd as g
+
+    x = workloads.paged_large_table_inputs(n_table=70000, n_pages=64, n_select=n_select, n_repeat=n_repeat,
+                                           seed=50 + n_select)
+    assert x.page_table.size * 4 > 262144
+    out, ws = _gpu(x, want_ws=True)
+    assert g.gqa_prefill_paged_sparse_dropped(ws) == n_repeat * 2
+    assert_parity(out, _oracle(x), f"table beyond the bitmap S={n_select}")
 
 
 def test_paged_empty_selection_gives_zero_rows():

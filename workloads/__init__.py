@@ -189,6 +189,42 @@ def paged_sparse_inputs(select_tokens: int, tail: int, seed: int, nq: int = 4096
     )
 
 
+def paged_large_table_inputs(n_table: int, n_pages: int, n_select: int, n_repeat: int, seed: int, nq: int = 128,
+                             page_size: int = PAGE_SIZE, hq: int = HQ, hkv: int = HKV,
+                             d: int = D) -> PagedSparseInputs:
+    """Paged inputs for a long request held in a small pool: n_table logical pages of
+    page_size tokens, each mapped to a physical page drawn at random from n_pages (pages are
+    shared, so the cache stays small).  The nq query rows are the last nq positions; each
+    query block selects its diagonal block plus n_select - 1 distinct random earlier blocks
+    spread over the whole table, then n_repeat copies of already selected ids inserted at
+    random places, in shuffled order."""
+    rng = np.random.default_rng(seed)
+    live_len = n_table * page_size
+    q_pos0 = live_len - nq
+    q = _normal16(rng, (nq, hq, d))
+    k_cache = _normal16(rng, (n_pages, page_size, hkv, d))
+    v_cache = _normal16(rng, (n_pages, page_size, hkv, d))
+    page_table = rng.integers(0, n_pages, size=n_table).astype(np.int32)
+    n_qblocks = -(-nq // QBLOCK_ROWS)
+    offsets, ids = [0], []
+    for b in range(n_qblocks):
+        diag = (q_pos0 + min(nq, (b + 1) * QBLOCK_ROWS) - 1) // KV_BLOCK_TOKENS
+        extra = rng.choice(diag, size=n_select - 1, replace=False)
+        sel = list(np.concatenate([[diag], extra]))
+        rng.shuffle(sel)
+        for r in rng.choice(sel, size=n_repeat, replace=True) if n_repeat else []:
+            sel.insert(int(rng.integers(0, len(sel) + 1)), r)
+        ids.append(np.asarray(sel, dtype=np.int64))
+        offsets.append(offsets[-1] + len(sel))
+    return PagedSparseInputs(
+        q=q, k_cache=k_cache, v_cache=v_cache, page_table=page_table,
+        qblock_offsets=np.asarray(offsets, dtype=np.int32),
+        kv_block_ids=np.concatenate(ids).astype(np.int32),
+        q_pos0=q_pos0, live_len=live_len, page_size=page_size,
+        meta=dict(n_table=n_table, n_pages=n_pages, n_select=n_select, n_repeat=n_repeat, seed=seed, nq=nq),
+    )
+
+
 # ------------------------------------------------------------ FP8 verifier tail
 VERIFY_CONTEXT = 261888
 E4M3_MAX = 448.0
