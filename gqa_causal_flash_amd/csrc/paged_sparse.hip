@@ -8,24 +8,27 @@
 // contributes only the tokens that exist.  Causal masking applies inside the
 // selection.
 //
-// Two kernels:
-//   paged_prepass  one workgroup of 512 threads per query block: bounds-checks each block id
-//                  and page, maps block x to its first physical cache row
-//                  page_table[x/(P/4)]*P + 4*(x%(P/4)) for pages of P tokens
-//                  (P a multiple of 4, so a 4-token block never straddles a
-//                  page: 16 and 784 in the pages' geometries), marks stale and invalid
-//                  blocks, sorts the list by physical row and drops
-//                  duplicates.
-//   paged_fwd      three workgroups per query block (128 packed rows each):
-//                  gathers 16 blocks (64 keys) per tile into the swizzled
-//                  double-buffered LDS tiles with direct-to-LDS loads (a
-//                  2 KiB contiguous block is two 1 KiB copies), records each
-//                  key's logical position, and runs the shared 32-key step
-//                  with the mask "position <= query position".  Slots of
-//                  stale or invalid entries are fetched at an offset past the
-//                  end of the cache buffer, so they read as zeros and never
-//                  bring NaN/Inf into the products; their position is
-//                  INT32_MAX, so they are never visible.
+// Three kernels:
+//   paged_prepass  one workgroup of 512 threads per query block: bounds-checks
+//                  each block id and page, maps block x to its first physical
+//                  cache row page_table[x/(P/4)]*P + 4*(x%(P/4)) for pages of P
+//                  tokens (P a multiple of 4, so a 4-token block never
+//                  straddles a page: 16 and 784 in the pages' geometries),
+//                  drops stale, invalid and repeated blocks and packs the rest
+//                  in logical order (a bitmap over the table's blocks: the
+//                  blocks of a page stay together, the locality the pages ask
+//                  of the fetch order).
+//   paged_fwd      teams of three workgroups (one per 128-row group of a query
+//                  block) over runs of equal cost: gathers 8 blocks (32 keys)
+//                  per sub-tile into swizzled double-buffered LDS tiles with
+//                  direct-to-LDS loads, records each key's logical position,
+//                  and runs the shared 32-key step with the mask "position <=
+//                  query position".  The padding slots of a query block's
+//                  last sub-tile are fetched at an offset past the end of the
+//                  cache buffer, so they read as zeros and never bring NaN/Inf
+//                  into the products; their position is INT32_MAX, so they
+//                  are never visible.
+//   paged_merge    combines the pieces of query blocks split between teams.
 #include "attn_common.hpp"
 #include "attn_tile.hpp"
 #include "launch.hpp"

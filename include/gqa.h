@@ -166,11 +166,13 @@ gqa_status gqa_prefill_causal_varlen_skipped(const void* workspace, int32_t* cou
  *            b*qblock_rows + qblock_rows - 1) selects the logical blocks
  *            kv_block_ids[qblock_offsets[b] .. qblock_offsets[b+1]-1]; block
  *            id x covers tokens x*kv_block_tokens .. x*kv_block_tokens +
- *            kv_block_tokens - 1.  Ids within a query block must be distinct;
- *            their order does not change the result.  Selections of up to
- *            2048 ids are sorted by cache address (a repeated id is then
- *            dropped and counted, see below); longer ones are used in the
- *            given order, where a repeated id is not detected and counts twice.
+ *            kv_block_tokens - 1.  A query block's selection is a set: its
+ *            order does not change the result, and a repeated id is dropped
+ *            and counted (see below).  The blocks are gathered in logical
+ *            order, which keeps the blocks of a page together.  For requests
+ *            of more than 262144 blocks (1M tokens) repeats are found only in
+ *            selections of up to 2048 ids; a longer selection there is used in
+ *            the given order and a repeated id in it counts twice.
  *   Row r of block b sees token j iff j lies in a selected block of b,
  *   j <= q_pos0 + r and j < live_len.  A row that sees nothing outputs 0.
  *   requires q_pos0 >= 0, q_pos0 + nq <= live_len <= n_table * page_size;
@@ -182,7 +184,8 @@ gqa_status gqa_prefill_causal_varlen_skipped(const void* workspace, int32_t* cou
  *   not on the host: a block id outside [0, n_table*page_size/kv_block_tokens),
  *   a physical page outside [0, n_pages) or a decreasing/out-of-range offset
  *   is dropped (it contributes nothing, no memory outside the arrays is
- *   touched) and counted; gqa_prefill_paged_sparse_dropped() reads the count.
+ *   touched) and counted, as is each repeated id; gqa_prefill_paged_sparse_dropped()
+ *   reads the count.
  * ------------------------------------------------------------------------ */
 gqa_status gqa_prefill_paged_sparse_workspace_size(int32_t nq, int32_t n_block_ids, int32_t qblock_rows,
                                                    int32_t kv_block_tokens, int32_t hq, int32_t hkv, int32_t d,
@@ -196,7 +199,7 @@ gqa_status gqa_prefill_paged_sparse(const void* q, const void* k_cache, const vo
                                     void* workspace, size_t workspace_bytes, void* stream);
 
 /* Number of index entries the last paged call that used `workspace` dropped
- * as invalid (see above).  Synchronises `stream`; host pointer `count`. */
+ * as invalid or repeated (see above).  Synchronises `stream`; host pointer `count`. */
 gqa_status gqa_prefill_paged_sparse_dropped(const void* workspace, int32_t* count, void* stream);
 
 /* ------------------------------------------------------------------------ *
