@@ -375,7 +375,9 @@ struct PagedSched {
 #pragma unroll
     for (int d = 32; d >= 1; d >>= 1) t += __shfl_xor(t, d);
     run.total = tot0 + __builtin_amdgcn_readfirstlane(t);
-    run.per = max((run.total + kPagedTeams - 1) / kPagedTeams, 2);
+    // a run shorter than a query block's start cost plus the smallest piece
+    // would hold little but that cost, and its team would sit idle
+    run.per = max((run.total + kPagedTeams - 1) / kPagedTeams, kPagedSwitchUnits + kPagedMinPiece);
     run.teams = (run.total + run.per - 1) / run.per;
   }
 
