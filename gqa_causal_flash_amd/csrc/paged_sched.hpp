@@ -2,16 +2,21 @@
 //
 // Query block b = 64 query tokens = 384 packed rows (token * 6 + head), handled
 // by three workgroups of 128 packed rows (4 waves x 32 rows).  Its selection
-// of 4-token KV blocks is translated, checked and sorted by physical address
-// by a prepass into the workspace:
+// of 4-token KV blocks is translated, checked, freed of repeats and packed by
+// a prepass into the workspace:
 //
 //   int32 header[4]   {magic, number of query blocks, number of ids, 0}
 //   int32 err[nqb]    index entries of block b dropped as invalid
 //   int32 beg[nqb]    first entry of block b in `entries`
-//   int32 cnt[nqb]    number of entries of block b (sorted valid ones first)
-//   int2  entries[n_block_ids]  {first physical cache row, first logical token}
-//                                or {-1, INT32_MAX} for an entry that holds no
-//                                live token
+//   int32 cnt[nqb]    number of entries of block b
+//   int32 nvis[nqb]   number of leading entries of block b that every row of
+//                     the block sees whole (entries ascending by token, all
+//                     four tokens at or before the block's first row); 0 when
+//                     the entries are in the given order
+//   int2  entries[n_block_ids]  {first physical cache row, first logical token};
+//                                a long selection over a table too large for
+//                                the prepass bitmap keeps {-1, INT32_MAX} in
+//                                place for an entry that holds no live token
 #pragma once
 
 #include <stddef.h>
@@ -50,7 +55,7 @@ constexpr int kPagedSlots = 2 * 3 * kPagedTeams;
 constexpr size_t kPagedSlotFloats = (size_t)kPagedRowsPerWG * 256 + 2 * kPagedRowsPerWG;
 
 struct PagedLayout {
-  size_t err, beg, cnt, entries, part, total;
+  size_t err, beg, cnt, nvis, entries, part, total;
 };
 
 inline PagedLayout paged_layout(int nqb, int n_ids) {
@@ -58,7 +63,8 @@ inline PagedLayout paged_layout(int nqb, int n_ids) {
   L.err = 16;
   L.beg = L.err + 4 * (size_t)nqb;
   L.cnt = L.beg + 4 * (size_t)nqb;
-  L.entries = (L.cnt + 4 * (size_t)nqb + 15) / 16 * 16;
+  L.nvis = L.cnt + 4 * (size_t)nqb;
+  L.entries = (L.nvis + 4 * (size_t)nqb + 15) / 16 * 16;
   L.part = (L.entries + 8 * (size_t)(n_ids > 0 ? n_ids : 1) + 255) / 256 * 256;
   L.total = L.part + (size_t)kPagedSlots * kPagedSlotFloats * 4;
   return L;

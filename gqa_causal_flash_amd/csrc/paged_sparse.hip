@@ -54,7 +54,7 @@ struct PagedParams {
   _Float16* o;
   char* ws;
   int n_table, n_pages, page_size, n_ids, nq, nrows, nqb, q_pos0, live_len;
-  size_t off_err, off_beg, off_cnt, off_entries, off_part;
+  uint32_t off_err, off_beg, off_cnt, off_nvis, off_entries, off_part;  // the workspace is below 4 GiB
   uint32_t part_bytes;
   float c;
 };
@@ -103,6 +103,7 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
   int* err = (int*)(p.ws + p.off_err);
   int* beg = (int*)(p.ws + p.off_beg);
   int* cnt = (int*)(p.ws + p.off_cnt);
+  int* nvis = (int*)(p.ws + p.off_nvis);
   int2* ent = (int2*)(p.ws + p.off_entries);
 
   if (tid == 0) errs = 0;
@@ -229,6 +230,13 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     if (tid == 0) {
       cnt[b] = total;
       beg[b] = start;
+      // blocks x < x_thr end at or before the query block's first row:
+      // 4x + 3 <= q_pos0 + 64b
+      const int first_pos = p.q_pos0 + b * kQBlockTokens;
+      const int x_thr = min((first_pos + 1) / kBlockTokens, words * 32);
+      const int wi = x_thr >> 5;
+      nvis[b] = wi >= words ? total
+                            : word_before[wi] + __popc(bits[wi] & ((1u << (x_thr & 31)) - 1u));
     }
   } else if (n <= kDedupMax) {
     // A table too large for the bitmap: repeats are found through an
@@ -290,6 +298,7 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     if (tid == 0) {
       cnt[b] = total;
       beg[b] = start;
+      nvis[b] = 0;
     }
   } else {
     // a long selection over a table too large for the bitmap: the given order,
@@ -304,6 +313,7 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     if (tid == 0) {
       cnt[b] = n;
       beg[b] = start;
+      nvis[b] = 0;
     }
   }
   __syncthreads();  // errs complete
@@ -531,6 +541,7 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
   const uint32_t vl = 512u * half + ((16u * col) ^ (64u * half));
   const int* cnt = (const int*)(p.ws + p.off_cnt);
   const int* begp = (const int*)(p.ws + p.off_beg);
+  const int* nvisp = (const int*)(p.ws + p.off_nvis);
   const int2* ent = (const int2*)(p.ws + p.off_entries);
   const PagedSched sched(cnt, p.nqb, lane);
   const PagedRun& run = sched.run;
@@ -592,6 +603,12 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
     // flight while x is computed.  The entries of x are loaded into set i % 2
     // two steps before the step that gathers with them (step x - 1), so a
     // gather never waits for its entries.
+    // Sub-tiles before x_mask hold only blocks that every row of the query
+    // block sees whole (the entries ascend by token), so they need no mask;
+    // the rest (the blocks near the diagonal, a part-filled last sub-tile,
+    // entries in the given order) take it, read from the key positions
+    // staged with the tile.
+    const int x_mask = max(s0, min(s1, __builtin_amdgcn_readfirstlane(nvisp[b]) / (kSubKeys / kBlockTokens)));
     SubEntries es[2];
     es[0] = sub_entries(ent, e_beg + 8 * s0, e_end, wave);
     issue(std::integral_constant<int, 0>{}, es[0]);
@@ -601,23 +618,13 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
     lds_barrier();
     auto step = [&](auto ic, int x) {
       constexpr int I = decltype(ic)::value;  // (x - s0) % 2
+      const bool mask = x >= x_mask;
       if (x + 1 < s1) issue(std::integral_constant<int, I ^ 1>{}, es[I ^ 1]);  // lands in the other slot
       es[I ^ 1] = sub_entries(ent, e_beg + 8 * (x + 3), e_end, wave);          // used two steps on
       // keep the per-lane bases opaque so derived addresses are formed here,
       // next to their use, instead of being hoisted and held in registers
       asm volatile("" : "+v"(bk), "+v"(bv));
       const int* kps = pslot(std::integral_constant<int, I>{});
-      // a sub-tile whose keys all sit at or before the wave's first row (the
-      // usual case: selections lie mostly far behind the query block) needs no
-      // mask; dead and stale slots carry INT32_MAX and force one.  Positions of
-      // this lane's keys: 4 runs of 4 at 8q + 4h.
-      int kmax = -1;
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int4 v4 = *(const int4*)&kps[8 * q4 + 4 * half];
-        kmax = max(kmax, max(max(v4.x, v4.y), max(v4.z, v4.w)));
-      }
-      const bool mask = !__all(kmax <= wpos_lo);
       auto visible = [&](int, int vv) { return kps[8 * (vv >> 2) + 4 * half + (vv & 3)] <= pos; };
       // two K fragments in flight instead of four: the registers go to the
       // schedule state, and no value of the loop is spilled
@@ -783,11 +790,12 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   p.q_pos0 = q_pos0;
   p.live_len = live_len;
   const PagedLayout L = paged_layout(p.nqb, n_block_ids);
-  p.off_err = L.err;
-  p.off_beg = L.beg;
-  p.off_cnt = L.cnt;
-  p.off_entries = L.entries;
-  p.off_part = L.part;
+  p.off_err = (uint32_t)L.err;
+  p.off_beg = (uint32_t)L.beg;
+  p.off_cnt = (uint32_t)L.cnt;
+  p.off_nvis = (uint32_t)L.nvis;
+  p.off_entries = (uint32_t)L.entries;
+  p.off_part = (uint32_t)L.part;
   p.part_bytes = (uint32_t)(L.total - L.part);
   p.c = scale * kLog2e;
   hipLaunchKernelGGL(paged_prepass, dim3(p.nqb), dim3(kPrepassThreads), 0, stream, p);

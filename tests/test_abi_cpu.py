@@ -149,11 +149,11 @@ def test_paged_rejects_before_launch(kw, status):
 @pytest.mark.parametrize("nq,n_ids", [(4096, 1000), (4096, 64 * 128), (4096, 64 * 512), (4096, 64 * 32),
                                        (128, 6048), (64, 1), (200000, 3125 * 512)])
 def test_paged_workspace_follows_the_layout(nq, n_ids):
-    """Restated: a 16-byte header, three int32 per 64-token query block (rounded up to 16 bytes), 8 bytes
+    """Restated: a 16-byte header, four int32 per 64-token query block (rounded up to 16 bytes), 8 bytes
     per id (rounded up to 256 bytes), then the partial slots: two per workgroup of the 168 teams of three
     that share the work, one fp32 partial of 128 rows (132096 bytes) each."""
     nqb = -(-nq // 64)
-    entries = -(-(16 + 12 * nqb) // 16) * 16
+    entries = -(-(16 + 16 * nqb) // 16) * 16
     part = -(-(entries + 8 * max(n_ids, 1)) // 256) * 256
     n = ctypes.c_size_t()
     assert g.lib().gqa_prefill_paged_sparse_workspace_size(nq, n_ids, 64, 4, 6, 1, 256, ctypes.byref(n)) == g.GQA_OK
