@@ -141,28 +141,49 @@ def _counter_rows(path: str, counter: str):
     return rows
 
 
+# kernel -> workload family, and the kernels a benchmark step of each family starts with
+KERNEL_FAMILY = {"prefill_causal_fwd": "prefill", "prefill_merge": "prefill",
+                 "paged_prepass": "paged", "paged_fwd": "paged", "paged_merge": "paged",
+                 "verify_fwd": "verify", "verify_merge": "verify",
+                 "prefill_varlen_prepass": "varlen", "prefill_causal_varlen": "varlen",
+                 "prefill_merge_varlen": "varlen", "prefill_causal_e4m3": "e4m3"}
+STEP_STARTS = {"prefill_causal_fwd", "paged_prepass", "verify_fwd", "prefill_varlen_prepass", "prefill_causal_e4m3"}
+
+
+def family_labels(n_kv: int) -> dict:
+    """The workloads of each family in the order main() runs them."""
+    prefill_paths = [workloads.TINY, workloads.LONG_40K] + [c for c in workloads.SWEEP if c.n_kv != n_kv]
+    return {"prefill": [prefill_workload(n_kv)] + [prefill_workload(c.n_kv, c.nq) for c in prefill_paths],
+            "varlen": [varlen_workload()], "e4m3": [e4m3_workload(128000)],
+            "paged": [paged_workload(s) for s in PAGED_SELECTIONS] + [paged_dense_workload(p) for p in PAGED_DENSE_PAGES],
+            "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
+
+
+def assign_workloads(rows, per: int, n_kv: int):
+    """Label (dispatch, kernel, value) rows of one default benchmark run with their workload.
+
+    A step starts at one of STEP_STARTS, and each workload of a family makes
+    `per` (warmup + steps) of them; kernels outside the families are dropped."""
+    labels = family_labels(n_kv)
+    count = {k: 0 for k in labels}
+    cur = None
+    for _, name, v in rows:
+        if name in STEP_STARTS:
+            cur = KERNEL_FAMILY[name]
+            count[cur] += 1
+        if cur is None or KERNEL_FAMILY.get(name) != cur:
+            continue
+        yield name, labels[cur][min((count[cur] - 1) // per, len(labels[cur]) - 1)], v
+
+
 def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, calib_mib: int, n_kv: int) -> str:
     """Markdown table of FETCH_SIZE / WRITE_SIZE per launch of every libgqa kernel.
 
     The three plain device copies of `calib_mib` MiB made before any workload are
     the known-size reference: each counter's scale factor is the copy's true byte
     count over what the counter reads for it.  Dispatches are assigned to
-    workloads by the benchmark's fixed order: a step starts at prefill_causal_fwd,
-    paged_prepass or verify_fwd, and each workload makes warmup + steps of them."""
+    workloads by the benchmark's fixed order (assign_workloads)."""
     per = warmup + steps
-    family = {"prefill_causal_fwd": "prefill", "prefill_merge": "prefill",
-              "paged_prepass": "paged", "paged_fwd": "paged", "paged_merge": "paged",
-              "verify_fwd": "verify", "verify_merge": "verify",
-              "prefill_varlen_prepass": "varlen", "prefill_causal_varlen": "varlen", "prefill_merge_varlen": "varlen",
-              "prefill_causal_e4m3": "e4m3"}
-    first = {"prefill_causal_fwd", "paged_prepass", "verify_fwd", "prefill_varlen_prepass",
-             "prefill_causal_e4m3"}  # a step starts here
-    # the order in which main() runs the workloads of each family
-    prefill_paths = [workloads.TINY, workloads.LONG_40K] + [c for c in workloads.SWEEP if c.n_kv != n_kv]
-    labels = {"prefill": [prefill_workload(n_kv)] + [prefill_workload(c.n_kv, c.nq) for c in prefill_paths],
-              "varlen": [varlen_workload()], "e4m3": [e4m3_workload(128000)],
-              "paged": [paged_workload(s) for s in PAGED_SELECTIONS] + [paged_dense_workload(p) for p in PAGED_DENSE_PAGES],
-              "verify": [verify_workload(q) for q in VERIFY_QUERIES]}
     true_kib = calib_mib * 1024.0
     result, factors = {}, {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -171,15 +192,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
         if len(copies) < 3 or max(copies) > 1.01 * min(copies):
             raise SystemExit(f"{path}: the first three copies do not look like the {calib_mib} MiB calibration: {copies}")
         factors[counter] = true_kib / (sum(copies) / 3)
-        count = {k: 0 for k in labels}
-        cur = None
-        for _, name, v in rows:
-            if name in first:
-                cur = family[name]
-                count[cur] += 1
-            if cur is None or family.get(name) != cur:
-                continue
-            wl = labels[cur][min((count[cur] - 1) // per, len(labels[cur]) - 1)]
+        for name, wl, v in assign_workloads(rows, per, n_kv):
             result.setdefault((name, wl), {}).setdefault(counter, []).append(v)
     lines = [
         "| kernel | workload | dispatches | FETCH_SIZE (KiB, avg) | WRITE_SIZE (KiB, avg) | HBM bytes per launch |",
@@ -194,6 +207,30 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
             f"calibration: plain device copy of {calib_mib} MiB; FETCH_SIZE scale {factors['FETCH_SIZE']:.4f}, "
             f"WRITE_SIZE scale {factors['WRITE_SIZE']:.4f}\n\n")
     return head + "\n".join(lines) + "\n"
+
+
+def summarize_trace(trace_csv: str, steps: int, warmup: int, n_kv: int) -> str:
+    """Markdown table of the duration of every libgqa kernel per workload, from a rocprofv3
+    --kernel-trace CSV of the default benchmark run with the given --steps/--warmup: average
+    over all dispatches and over the timed ones (the last `steps` of each workload), min, max."""
+    per = warmup + steps
+    rows = []
+    with open(trace_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"gqa::\(anonymous namespace\)::(\w+)", r["Kernel_Name"])
+            if m:
+                rows.append((int(r["Dispatch_Id"]), m.group(1), int(r["End_Timestamp"]) - int(r["Start_Timestamp"])))
+    rows.sort()
+    result = {}
+    for name, wl, d in assign_workloads(rows, per, n_kv):
+        result.setdefault((name, wl), []).append(d)
+    lines = ["| kernel | workload | dispatches | average (us) | timed average (us) | min (us) | max (us) |",
+             "|---|---|---|---|---|---|---|"]
+    for (name, wl), ds in result.items():
+        timed = ds[-steps:]
+        lines.append(f"| `{name}` | `{wl}` | {len(ds)} | {sum(ds) / len(ds) / 1e3:,.1f} | "
+                     f"{sum(timed) / len(timed) / 1e3:,.1f} | {min(ds) / 1e3:,.1f} | {max(ds) / 1e3:,.1f} |")
+    return "\n".join(lines) + "\n"
 
 
 def summarize_sweep_trace(trace_csv: str, steps: int, warmup: int) -> str:
@@ -585,10 +622,17 @@ def main(argv=None):
     ap.add_argument("--summarize-sweep-trace", metavar="TRACE_CSV",
                     help="print the per-point kernel times of a rocprofv3 --kernel-trace CSV of a --sweep run made "
                          "with the given --steps/--warmup, and exit")
+    ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
+                    help="print the per-workload kernel times of a rocprofv3 --kernel-trace CSV of a default run "
+                         "made with the given --steps/--warmup/--kv, and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-launch HBM traffic table from two rocprofv3 --pmc counter_collection.csv "
                          "files of a run made with the given --steps/--warmup/--kv/--copy-calibration-mib, and exit")
     args = ap.parse_args(argv)
+
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.kv), end="")
+        return 0
 
     if args.summarize_sweep_trace:
         print(summarize_sweep_trace(args.summarize_sweep_trace, args.steps, args.warmup), end="")
