@@ -209,6 +209,31 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
     return head + "\n".join(lines) + "\n"
 
 
+def summarize_metrics(counter_csv: str, steps: int, warmup: int, n_kv: int) -> str:
+    """Markdown table of every counter or derived metric of one rocprofv3 --pmc counter_collection.csv
+    of the default benchmark (run with the given --steps/--warmup/--kv), averaged per kernel and workload."""
+    per = warmup + steps
+    by_counter = {}
+    with open(counter_csv, newline="") as f:
+        for r in csv.DictReader(f):
+            m = re.search(r"gqa::\(anonymous namespace\)::(\w+)", r["Kernel_Name"])
+            if m:
+                by_counter.setdefault(r["Counter_Name"], []).append(
+                    (int(r["Dispatch_Id"]), m.group(1), float(r["Counter_Value"])))
+    names = list(by_counter)
+    result = {}
+    for cn, rows in by_counter.items():
+        rows.sort()
+        for name, wl, v in assign_workloads(rows, per, n_kv):
+            result.setdefault((name, wl), {}).setdefault(cn, []).append(v)
+    lines = ["| kernel | workload | dispatches | " + " | ".join(names) + " |",
+             "|---|---|---|" + "---|" * len(names)]
+    for (name, wl), c in result.items():
+        vals = [sum(c.get(n, [0.0])) / max(1, len(c.get(n, []))) for n in names]
+        lines.append(f"| `{name}` | `{wl}` | {len(c.get(names[0], []))} | " + " | ".join(f"{v:.2f}" for v in vals) + " |")
+    return "\n".join(lines) + "\n"
+
+
 def summarize_trace(trace_csv: str, steps: int, warmup: int, n_kv: int) -> str:
     """Markdown table of the duration of every libgqa kernel per workload, from a rocprofv3
     --kernel-trace CSV of the default benchmark run with the given --steps/--warmup: average
@@ -625,6 +650,9 @@ def main(argv=None):
     ap.add_argument("--summarize-trace", metavar="TRACE_CSV",
                     help="print the per-workload kernel times of a rocprofv3 --kernel-trace CSV of a default run "
                          "made with the given --steps/--warmup/--kv, and exit")
+    ap.add_argument("--summarize-metrics", metavar="COUNTER_CSV",
+                    help="print every counter of a rocprofv3 --pmc counter_collection.csv of a default run made "
+                         "with the given --steps/--warmup/--kv, averaged per kernel and workload, and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="print the per-launch HBM traffic table from two rocprofv3 --pmc counter_collection.csv "
                          "files of a run made with the given --steps/--warmup/--kv/--copy-calibration-mib, and exit")
@@ -632,6 +660,10 @@ def main(argv=None):
 
     if args.summarize_trace:
         print(summarize_trace(args.summarize_trace, args.steps, args.warmup, args.kv), end="")
+        return 0
+
+    if args.summarize_metrics:
+        print(summarize_metrics(args.summarize_metrics, args.steps, args.warmup, args.kv), end="")
         return 0
 
     if args.summarize_sweep_trace:
