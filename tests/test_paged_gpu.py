@@ -231,6 +231,40 @@ def test_paged_table_beyond_the_bitmap(n_select, n_repeat):
     assert_parity(out, _oracle(x), f"table beyond the bitmap S={n_select}")
 
 
+def _subselect(x, counts, seed):
+    """Per query block b, counts[b % len(counts)] distinct blocks drawn from the block's full causal
+    selection (x built with saturate=True), in shuffled order."""
+    rng = np.random.default_rng(seed)
+    offs = x.qblock_offsets
+    ids, new_offs = [], [0]
+    for b in range(offs.size - 1):
+        full = x.kv_block_ids[offs[b]:offs[b + 1]]
+        k = min(counts[b % len(counts)], full.size)
+        sel = rng.choice(full, size=k, replace=False) if k else np.zeros(0, dtype=np.int32)
+        ids += [int(i) for i in sel]
+        new_offs.append(len(ids))
+    return np.asarray(ids, dtype=np.int32), np.asarray(new_offs, dtype=np.int32)
+
+
+def test_paged_mixed_selection_lengths():
+    """Selections of 0 to 1000 blocks mixed across 64 query blocks: empty query blocks between
+    selected ones, single-block and part-filled sub-tiles, runs cut inside long blocks and boundaries
+    moved to block ends."""
+    x = workloads.paged_sparse_inputs(select_tokens=4, tail=2, seed=60, saturate=True)
+    ids, offs = _subselect(x, [0, 1, 3, 8, 9, 16, 17, 64, 100, 511, 512, 513, 1000, 2, 0, 7], seed=61)
+    assert (np.diff(offs) == 0).sum() >= 4
+    assert_parity(_gpu(x, ids=ids, offs=offs), _oracle(x, ids=ids, offs=offs), "mixed selection lengths")
+
+
+def test_paged_one_long_query_block_among_short_ones():
+    """The last query block selects all of its 1024 blocks and every other one a single block, so the
+    runs are at their shortest and the long block is split into about 26 pieces for the merge."""
+    x = workloads.paged_sparse_inputs(select_tokens=4, tail=1, seed=62, saturate=True)
+    ids, offs = _subselect(x, [1] * 63 + [4096], seed=63)
+    assert np.diff(offs)[-1] == 1025
+    assert_parity(_gpu(x, ids=ids, offs=offs), _oracle(x, ids=ids, offs=offs), "one long query block")
+
+
 def test_paged_empty_selection_gives_zero_rows():
     x = workloads.paged_sparse_inputs(select_tokens=64, tail=0, seed=15, nq=128)
     offs = np.array([0, 0, x.qblock_offsets[2] - x.qblock_offsets[1]], dtype=np.int32)
