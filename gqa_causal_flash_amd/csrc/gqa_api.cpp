@@ -64,8 +64,10 @@ thread_local Profiler g_prof;
 hipEvent_t prof_event() {
   const size_t used = g_prof.marks.size();
   if (used < g_prof.pool.size()) return g_prof.pool[used];
+  // timing only: no system-scope fence at record time (no cache write-back
+  // and invalidation between the kernels being timed)
   hipEvent_t e = nullptr;
-  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  if (hipEventCreateWithFlags(&e, hipEventDisableSystemFence) != hipSuccess) return nullptr;
   g_prof.pool.push_back(e);
   return e;
 }
@@ -73,21 +75,22 @@ hipEvent_t prof_event() {
 }  // namespace
 
 namespace gqa {
-void prof_before(hipStream_t stream) {
-  if (!g_prof.on) return;
-  hipEvent_t e = prof_event();
-  if (e && hipEventRecord(e, stream) == hipSuccess) g_prof.marks.push_back(e);
+bool prof_events(hipEvent_t* start, hipEvent_t* stop) {
+  if (!g_prof.on) return false;
+  hipEvent_t a = prof_event();
+  if (!a) return false;
+  g_prof.marks.push_back(a);
+  hipEvent_t b = prof_event();
+  if (!b) {
+    g_prof.marks.pop_back();  // no pair: this launch goes untimed
+    return false;
+  }
+  g_prof.marks.push_back(b);
+  *start = a;
+  *stop = b;
+  return true;
 }
 unsigned long long* prof_clock() { return g_prof.on ? g_prof.clk : nullptr; }
-void prof_after(hipStream_t stream) {
-  if (!g_prof.on || g_prof.marks.size() % 2 == 0) return;
-  hipEvent_t e = prof_event();
-  if (e && hipEventRecord(e, stream) == hipSuccess) {
-    g_prof.marks.push_back(e);
-  } else {
-    g_prof.marks.pop_back();  // drop the unmatched start
-  }
-}
 }  // namespace gqa
 
 extern "C" {

@@ -9,10 +9,26 @@
 
 namespace gqa {
 
-// Kernel timing hook (see gqa_profile_start): the launchers bracket their main
-// attention kernel with these; both are no-ops unless profiling is on.
-void prof_before(hipStream_t stream);
-void prof_after(hipStream_t stream);
+// Kernel timing hook (see gqa_profile_start): while profiling is on, hands out
+// a start/stop event pair for the next main-kernel launch and returns true.
+bool prof_events(hipEvent_t* start, hipEvent_t* stop);
+
+// Launches a library kernel; the main attention kernel of each entry point goes
+// through here.  While profiling, the launch is bracketed by a pair of events
+// recorded on the stream (created without the system-scope fence, so a record
+// does not write back and invalidate the caches).
+template <class Kernel, class Params>
+hipError_t launch_timed(Kernel kernel, dim3 grid, dim3 block, hipStream_t stream, const Params& p) {
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  const bool timed = prof_events(&e0, &e1);
+  hipError_t e = timed ? hipEventRecord(e0, stream) : hipSuccess;
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kernel, grid, block, 0, stream, p);
+  e = hipGetLastError();
+  if (e != hipSuccess || !timed) return e;
+  return hipEventRecord(e1, stream);
+}
+
 // Device accumulator {shader clock cycles, wall-clock ticks} that the prefill
 // kernel adds its workgroups' lifetimes to while profiling is on, else null.
 unsigned long long* prof_clock();

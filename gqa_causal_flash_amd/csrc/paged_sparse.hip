@@ -801,10 +801,7 @@ hipError_t launch_paged_sparse(const void* q, const void* k_cache, const void* v
   hipLaunchKernelGGL(paged_prepass, dim3(p.nqb), dim3(kPrepassThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  prof_before(stream);
-  hipLaunchKernelGGL(paged_fwd, dim3(kPagedGrid), dim3(64 * kWaves), 0, stream, p);
-  e = hipGetLastError();
-  prof_after(stream);
+  e = launch_timed(paged_fwd, dim3(kPagedGrid), dim3(64 * kWaves), stream, p);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(paged_merge, dim3(p.nqb * kPagedWGsPerQBlock * kMergeWGsPerRowGroup), dim3(256), 0, stream, p);
   return hipGetLastError();

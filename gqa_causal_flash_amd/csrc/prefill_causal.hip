@@ -748,10 +748,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.clk = prof_clock();
   p.lse = nullptr;
   p.vdesc = nullptr;
-  prof_before(stream);
-  hipLaunchKernelGGL((prefill_causal_fwd<kPrefillC, kPrefillW>), dim3(s.grid), dim3(64 * kPrefillW), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  prof_after(stream);
+  hipError_t e = launch_timed(prefill_causal_fwd<kPrefillC, kPrefillW>, dim3(s.grid), dim3(64 * kPrefillW), stream, p);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
     hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
@@ -783,10 +780,7 @@ hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* 
   p.clk = prof_clock();
   p.lse = nullptr;
   p.vdesc = nullptr;
-  prof_before(stream);
-  hipLaunchKernelGGL(prefill_causal_e4m3, dim3(s.grid), dim3(512), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  prof_after(stream);
+  hipError_t e = launch_timed(prefill_causal_e4m3, dim3(s.grid), dim3(512), stream, p);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
     hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
@@ -830,10 +824,7 @@ hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void
   p.clk = nullptr;
   p.lse = lse;
   p.vdesc = pre.desc;
-  prof_before(stream);
-  hipLaunchKernelGGL(prefill_causal_varlen, dim3(p.grid), dim3(512), 0, stream, p);
-  e = hipGetLastError();
-  prof_after(stream);
+  e = launch_timed(prefill_causal_varlen, dim3(p.grid), dim3(512), stream, p);
   if (e != hipSuccess || vs.split == 1) return e;
   hipLaunchKernelGGL(prefill_merge_varlen, dim3(vs.cap * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
   return hipGetLastError();

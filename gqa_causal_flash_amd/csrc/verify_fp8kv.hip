@@ -390,13 +390,8 @@ hipError_t launch_verify_fp8kv(const void* q, const uint8_t* k, const uint8_t* v
   p.part_bytes = (uint32_t)verify_workspace_bytes(s);
   p.c = scale * k_scale * kLog2e;
   p.v_scale = v_scale;
-  prof_before(stream);
-  if (s.row_blocks == 1)
-    hipLaunchKernelGGL(verify_fwd<1>, dim3(s.grid), dim3(128), 0, stream, p);
-  else
-    hipLaunchKernelGGL(verify_fwd<2>, dim3(s.grid), dim3(256), 0, stream, p);
-  hipError_t e = hipGetLastError();
-  prof_after(stream);
+  hipError_t e = s.row_blocks == 1 ? launch_timed(verify_fwd<1>, dim3(s.grid), dim3(128), stream, p)
+                                    : launch_timed(verify_fwd<2>, dim3(s.grid), dim3(256), stream, p);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(verify_merge, dim3(p.nrows * 4), dim3(16 * kMergeLanes), 0, stream, p);
   return hipGetLastError();

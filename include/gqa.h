@@ -255,7 +255,9 @@ gqa_status gqa_verify_fp8kv_noalloc(const void* q, const uint8_t* k_e4m3, const 
  * Between gqa_profile_start() and gqa_profile_stop() on one host thread, every
  * successful call made by that thread records a pair of HIP events on its
  * stream around its main attention kernel (the one that reads K/V; merge and
- * index kernels are excluded).  gqa_profile_stop() waits for those events and
+ * index kernels are excluded).  The events are timing-only
+ * (hipEventDisableSystemFence: recording them writes back no cache).
+ * gqa_profile_stop() waits for those events and
  * returns the summed kernel time in milliseconds and the number of kernels
  * timed; it returns GQA_ERR_INVALID when profiling was not started.  This is
  * the only state the library keeps between calls; it is per thread and holds
