@@ -41,8 +41,9 @@ namespace gqa {
 namespace {
 
 constexpr int kWaves = 4;
-constexpr int kPrepassThreads = 512;  // sort lanes of the prepass (one workgroup per query block)
+constexpr int kPrepassThreads = 512;  // threads of the prepass (one workgroup per query block)
 constexpr uint32_t kNoRow = 0xFFFFFFF0u;  // buffer offset past any cache: reads zeros
+constexpr int kDeadToken = 0x7FFFFFFF;    // position of a slot that holds nothing live
 
 struct PagedParams {
   const _Float16* q;
@@ -307,7 +308,7 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
     for (int i = tid; i < n; i += kPrepassThreads) {
       const int x = load_id(i);
       const int2 t = translate(i, x, load_page(i, x), bad);
-      ent[start + i] = t.x < 0 ? int2{-1, 0x7FFFFFFF} : t;
+      ent[start + i] = t.x < 0 ? int2{-1, kDeadToken} : t;
     }
     if (bad) atomicAdd(&errs, bad);
     if (tid == 0) {
@@ -323,7 +324,6 @@ __global__ __launch_bounds__(kPrepassThreads) void paged_prepass(PagedParams p) 
 // ------------------------------------------------------------------ attention
 constexpr int kSubKeys = 32;                     // keys per sub-tile = 8 blocks
 constexpr int kSubBytes = kSubKeys * kRowBytes;  // 16 KiB for K or V
-constexpr int kDeadToken = 0x7FFFFFFF;           // token of an entry that holds nothing live
 // s_waitcnt vmcnt(0) (other counters untouched) as an instruction the compiler
 // sees: its own wait insertion then knows that every load has landed
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -340,12 +340,11 @@ constexpr int kWaitVmcnt0 = 0x0F70;
 // XCD's L2.  Every compute unit gets about the same work whatever the
 // selection lengths.  A boundary t * per that would cut fewer than
 // kPagedMinPiece sub-tiles off a query block moves to that block's start or
-// end (PagedSched::bound), so small query blocks stay whole.  A run covers the tail
-// of one query block, whole query blocks and the head of another: whole ones
-// are written straight to O, and
-// the (at most two) cut ones leave a partial of the row group in the
-// workgroup's slots 2w (its first query block) and 2w + 1 (its last), with
-// w = 3 team + g, which paged_merge combines.
+// end (PagedSched::bound), so small query blocks stay whole.  A run covers the
+// tail of one query block, whole query blocks and the head of another: whole
+// ones are written straight to O, and the (at most two) cut ones leave a
+// partial of the row group in the workgroup's slots 2w (its first query block)
+// and 2w + 1 (its last), with w = 3 team + g, which paged_merge combines.
 __device__ __forceinline__ int paged_nsub(const int* cnt, int b) { return (cnt[b] + 7) >> 3; }
 __device__ __forceinline__ int paged_weight(const int* cnt, int b) {
   const int n = paged_nsub(cnt, b);
@@ -466,7 +465,7 @@ struct PagedSched {
 // j = 4(w%2) + i, which gives the lane offsets kl ^ 32j (K) and
 // vl ^ 128(j%4) (V) used by the dense kernel, shifted to the entry's
 // physical row.  Lanes 0..7 also record the logical position of row 8w+l.
-// The wave's two entries (2w, 2w+1 of the sub-tile) are loaded a sub-tile
+// The wave's two entries (2w, 2w+1 of the sub-tile) are loaded two sub-tiles
 // ahead by sub_entries(), so the gather addresses do not wait on them.
 struct SubEntries {
   int2 e[2];
@@ -487,7 +486,7 @@ __device__ __forceinline__ SubEntries sub_entries(const int2* ent, int e0, int e
     if (e < e_end) {
       s.e[k] = int2{cent[2 * e], cent[2 * e + 1]};
     } else {
-      s.e[k] = int2{-1, 0x7FFFFFFF};
+      s.e[k] = int2{-1, kDeadToken};
     }
   }
   return s;
@@ -514,7 +513,7 @@ __device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk,
     const int2 en = lane < 4 ? se.e[0] : se.e[1];
     const int u = lane & 3;
     const bool live = en.x >= 0 && en.y + u < p.live_len;
-    kpos[8 * wave + lane] = live ? en.y + u : 0x7FFFFFFF;
+    kpos[8 * wave + lane] = live ? en.y + u : kDeadToken;
   }
 }
 
