@@ -137,6 +137,17 @@ def test_paged_page784_parity(select, tail):
     assert_parity(_gpu(x), _oracle(x), f"page 784 S={select} t={tail}")
 
 
+@pytest.mark.parametrize("page_size,select,tail", [(4, 512, 1), (12, 64, 3), (100, 2048, 2), (4096, 512, 0)])
+def test_paged_page_size_extremes(page_size, select, tail):
+    """Page sizes at both ends of the accepted range (one 4-token block per page, and 4096
+    tokens per page) and two that are not powers of two, over 1000 query rows (short last
+    query block)."""
+    x = workloads.paged_sparse_inputs(select_tokens=select, tail=tail, seed=500 + page_size, nq=1000,
+                                      page_size=page_size)
+    assert x.k_cache.shape[1] == page_size
+    assert_parity(_gpu(x), _oracle(x), f"page {page_size} S={select} t={tail}")
+
+
 @pytest.mark.parametrize("page_size", [16, 784])
 def test_paged_dense_causal_full_size(page_size):
     """Paged dense causal prefill (every block up to the diagonal selected), 4096 rows, against
