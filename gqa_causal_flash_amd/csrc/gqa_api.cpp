@@ -172,8 +172,7 @@ gqa_status gqa_prefill_causal_workspace_size(int32_t nq, int32_t n_kv, int32_t q
   if (!bytes) return GQA_ERR_INVALID;
   gqa_status st = prefill_sizes(nq, n_kv, q_pos0, hq, hkv, d);
   if (st != GQA_OK) return st;
-  const gqa::PrefillSched s = gqa::prefill_schedule(nq, hq, q_pos0);
-  const size_t w = gqa::prefill_workspace_bytes(s);
+  const size_t w = gqa::prefill_any_workspace_bytes(nq, hq, q_pos0);
   if ((int64_t)w > kMaxBufferBytes) return GQA_ERR_UNSUPPORTED;
   *bytes = w;
   return GQA_OK;

@@ -14,8 +14,10 @@
 // Each wave keeps its 32 rows of Q as matrix-core B fragments in registers
 // (16 steps of 16 head-dim columns) and its O^T accumulator (8 tiles of 32x32
 // fp32).  K/V tiles of 64 keys stream HBM -> LDS by direct-to-LDS loads into a
-// double buffer (2 x 64 KiB).  (Templates C and W give other row splits,
-// 32C rows per wave and W waves; the default is C = 1, W = 8.)
+// double buffer (2 x 64 KiB).  Small workloads take q-blocks of 128 rows:
+// four waves, one per SIMD, with the same per-wave work.  (Templates C and W
+// give other row splits, 32C rows per wave and W waves; the default is C = 1,
+// W = 8, or W = 4 for 128-row q-blocks.)
 #include "attn_common.hpp"
 #include "attn_tile.hpp"
 #include "prefill_sched.hpp"
@@ -28,12 +30,14 @@ namespace gqa {
 namespace {
 
 constexpr int kTileBytes = kTileKeys * kRowBytes;  // 32 KiB per K or V tile
-// Rows per wave = 32 * kPrefillC, waves per workgroup = kPrefillW.
+// Rows per wave = 32 * kPrefillC, waves per workgroup = kPrefillW (256-row
+// q-blocks) or kSmallW (128-row q-blocks).
 #ifndef GQA_PREFILL_C
 #define GQA_PREFILL_C 1
 #endif
 constexpr int kPrefillC = GQA_PREFILL_C;
 constexpr int kPrefillW = kRowsPerBlock / (32 * kPrefillC);
+constexpr int kSmallW = kRowsSmall / (32 * kPrefillC);
 
 struct PrefillParams {
   const _Float16* q;
@@ -42,6 +46,7 @@ struct PrefillParams {
   _Float16* o;
   float* part;
   int nrows;
+  int qrows;    // packed rows per q-block (and per partial slot)
   int kv_live;  // keys 0 .. kv_live-1 can be visible (q_pos0 + nq)
   int q_pos0;
   int nqb;
@@ -102,17 +107,14 @@ __device__ __forceinline__ void issue_tile(rsrc_t rk, rsrc_t rv, int tile, char*
   issue_rows<W>(rk, rv, (uint32_t)tile * (kTileKeys * kRowBytes), kdst, vdst, wave, kl, vl);
 }
 
-// Partial slot layout (fp32): acc[64 column quads][256 rows][4], m[256], l[256].
-constexpr int kPartM = kRowsPerBlock * kHeadDim;
-constexpr int kPartL = kPartM + kRowsPerBlock;
-
 // One piece of work: tiles tile_lo .. tile_hi-1 of q-block b, with W waves
-// of 32*C packed rows each (32*C*W = 256).
+// of 32*C packed rows each (32*C*W = the q-block's rows, p.qrows).
 template <int C, int W>
 __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem, int b, int tile_lo, int tile_hi,
                                               bool full, int slot) {
   constexpr int kRowsPerWave = 32 * C;
-  static_assert(kRowsPerWave * W == kRowsPerBlock, "a workgroup covers one q-block");
+  constexpr int kRows = kRowsPerWave * W;
+  static_assert(kRows == kRowsPerBlock || kRows == kRowsSmall, "a workgroup covers one q-block");
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -126,7 +128,7 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
   const rsrc_t rk = make_rsrc(p.k, (uint32_t)p.kv_live * kRowBytes);
   const rsrc_t rv = make_rsrc(p.v, (uint32_t)p.kv_live * kRowBytes);
 
-  const int row_base = b * kRowsPerBlock + wave * kRowsPerWave;
+  const int row_base = b * kRows + wave * kRowsPerWave;
   const bool wave_active = row_base < p.nrows;
   const int wrow_hi = min(row_base + kRowsPerWave - 1, p.nrows - 1);
   const int wpos_lo = p.q_pos0 + row_base / kGroup;
@@ -209,10 +211,10 @@ __device__ __forceinline__ void prefill_piece(const PrefillParams& p, char* smem
     }
   } else {
     const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-    const uint32_t sbase = (uint32_t)slot * (uint32_t)(kPartialFloats * 4);
+    const uint32_t sbase = (uint32_t)slot * (uint32_t)(prefill_partial_floats(kRows) * 4);
 #pragma unroll
     for (int c = 0; c < C; ++c)
-      store_partial(rp, sbase, kRowsPerBlock, wave * kRowsPerWave + 32 * c + col, half, acc[c], m[c], lt[c]);
+      store_partial(rp, sbase, kRows, wave * kRowsPerWave + 32 * c + col, half, acc[c], m[c], lt[c]);
   }
 }
 
@@ -224,7 +226,7 @@ __device__ __forceinline__ void prefill_workgroup(const PrefillParams& p, Run ru
   // q-blocks are dispatched last first: they are the longest, so the
   // shortest pieces end the kernel
   const int b = p.nqb - 1 - w / p.split, j = w % p.split;
-  const int nt = prefill_block_tiles(b, p.nrows, p.q_pos0);
+  const int nt = prefill_block_tiles(b, p.qrows, p.nrows, p.q_pos0);
   const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
   // the split never exceeds the shortest q-block's tile count, so lo < hi
   run(b, lo, hi, p.split == 1, b * p.split + j);
@@ -515,18 +517,20 @@ constexpr int kMergeThreadsPerRow = kHeadDim / kMergeCols;  // 8
 constexpr int kMergeRowsPerWG = 256 / kMergeThreadsPerRow;  // 32
 
 template <int G>
-__device__ __forceinline__ void merge_group(rsrc_t rp, int w0, int rl, int dq, float M, f4 (&o)[8], float& L) {
-  const uint32_t slot_bytes = (uint32_t)(kPartialFloats * 4);
+__device__ __forceinline__ void merge_group(rsrc_t rp, int rows, int w0, int rl, int dq, float M, f4 (&o)[8],
+                                            float& L) {
+  const uint32_t slot_bytes = (uint32_t)(prefill_partial_floats(rows) * 4);
+  const uint32_t part_m = (uint32_t)(rows * kHeadDim + rl) * 4, part_l = part_m + rows * 4;
   float mw[G], lw[G];
   u4 x[G][8];
 #pragma unroll
   for (int i = 0; i < G; ++i) {
     const uint32_t sb = (uint32_t)(w0 + i) * slot_bytes;
-    mw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartM + rl) * 4, 0, 0));
-    lw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + (kPartL + rl) * 4, 0, 0));
+    mw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + part_m, 0, 0));
+    lw[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rp, sb + part_l, 0, 0));
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((8 * dq + j) * kRowsPerBlock + rl) * 16), 0, 0);
+      x[i][j] = __builtin_amdgcn_raw_buffer_load_b128(rp, sb + (uint32_t)(((8 * dq + j) * rows + rl) * 16), 0, 0);
   }
   __builtin_amdgcn_sched_barrier(0);  // keep every load of the group ahead of the sums
 #pragma unroll
@@ -540,14 +544,16 @@ __device__ __forceinline__ void merge_group(rsrc_t rp, int w0, int rl, int dq, f
 
 __device__ __forceinline__ void merge_row(const PrefillParams& p, int slot_lo, int slot_hi, int rl, int dq, int orow) {
   const rsrc_t rp = make_rsrc(p.part, p.part_bytes);
-  const uint32_t slot_bytes = (uint32_t)(kPartialFloats * 4);
+  const int rows = p.qrows;
+  const uint32_t slot_bytes = (uint32_t)(prefill_partial_floats(rows) * 4);
+  const uint32_t part_m = (uint32_t)(rows * kHeadDim + rl) * 4;
   float M = -INFINITY;
   for (int w0 = slot_lo; w0 <= slot_hi; w0 += 8) {
     float mv[8];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
       mv[i] = __uint_as_float(
-          __builtin_amdgcn_raw_buffer_load_b32(rp, min(w0 + i, slot_hi) * slot_bytes + (kPartM + rl) * 4, 0, 0));
+          __builtin_amdgcn_raw_buffer_load_b32(rp, min(w0 + i, slot_hi) * slot_bytes + part_m, 0, 0));
 #pragma unroll
     for (int i = 0; i < 8; ++i) M = fmaxf(M, mv[i]);
   }
@@ -556,12 +562,12 @@ __device__ __forceinline__ void merge_row(const PrefillParams& p, int slot_lo, i
   for (int j = 0; j < 8; ++j) o[j] = f4{0.f, 0.f, 0.f, 0.f};
   float L = 0.f;
   int w0 = slot_lo;
-  for (; w0 + 3 <= slot_hi; w0 += 4) merge_group<4>(rp, w0, rl, dq, M, o, L);
+  for (; w0 + 3 <= slot_hi; w0 += 4) merge_group<4>(rp, rows, w0, rl, dq, M, o, L);
   if (w0 + 1 <= slot_hi) {
-    merge_group<2>(rp, w0, rl, dq, M, o, L);
+    merge_group<2>(rp, rows, w0, rl, dq, M, o, L);
     w0 += 2;
   }
-  if (w0 <= slot_hi) merge_group<1>(rp, w0, rl, dq, M, o, L);
+  if (w0 <= slot_hi) merge_group<1>(rp, rows, w0, rl, dq, M, o, L);
   const float inv = L > 0.f ? 1.0f / L : 0.f;
   const rsrc_t ro = make_rsrc(p.o, (uint32_t)p.nrows * kRowBytes);
   const uint32_t obase = (uint32_t)orow * kRowBytes + 2 * kMergeCols * dq;
@@ -580,14 +586,14 @@ __device__ __forceinline__ void merge_row(const PrefillParams& p, int slot_lo, i
 
 // Workgroup (b, part): 32 rows of q-block b; thread (row, 32 columns).
 __global__ __launch_bounds__(256) void prefill_merge(PrefillParams p) {
-  constexpr int kParts = kRowsPerBlock / kMergeRowsPerWG;
-  const int b = blockIdx.x / kParts;
-  const int part = blockIdx.x % kParts;
+  const int parts = p.qrows / kMergeRowsPerWG;
+  const int b = blockIdx.x / parts;
+  const int part = blockIdx.x % parts;
   // the pieces of q-block b are slots b*split .. b*split + split - 1 (the
   // merge runs only when split > 1)
   const int tid = threadIdx.x;
   const int rl = part * kMergeRowsPerWG + tid % kMergeRowsPerWG;
-  merge_row(p, b * p.split, b * p.split + p.split - 1, rl, tid / kMergeRowsPerWG, b * kRowsPerBlock + rl);
+  merge_row(p, b * p.split, b * p.split + p.split - 1, rl, tid / kMergeRowsPerWG, b * p.qrows + rl);
 }
 
 // ------------------------------------------------------------------ varlen
@@ -696,7 +702,7 @@ __global__ __launch_bounds__(512, 1) void prefill_causal_varlen(PrefillParams p)
   PrefillParams s;
   int jblk;
   if (!varlen_block(p, qb, s, jblk)) return;
-  const int nt = prefill_block_tiles(jblk, s.nrows, s.q_pos0);
+  const int nt = prefill_block_tiles(jblk, kRowsPerBlock, s.nrows, s.q_pos0);
   const int lo = (int)((long long)j * nt / p.split), hi = (int)((long long)(j + 1) * nt / p.split);
   if (lo >= hi) {  // a short q-block has fewer tiles than pieces: leave the empty state
     const int tid = threadIdx.x, lane = tid & 63;
@@ -736,6 +742,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.o = (_Float16*)o;
   p.part = (float*)workspace;
   p.nrows = s.nrows;
+  p.qrows = s.rows;
   p.kv_live = q_pos0 + nq;
   (void)n_kv;
   p.q_pos0 = q_pos0;
@@ -748,10 +755,13 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
   p.clk = prof_clock();
   p.lse = nullptr;
   p.vdesc = nullptr;
-  hipError_t e = launch_timed(prefill_causal_fwd<kPrefillC, kPrefillW>, dim3(s.grid), dim3(64 * kPrefillW), stream, p);
+  hipError_t e = s.rows == kRowsSmall
+                     ? launch_timed(prefill_causal_fwd<kPrefillC, kSmallW>, dim3(s.grid), dim3(64 * kSmallW), stream, p)
+                     : launch_timed(prefill_causal_fwd<kPrefillC, kPrefillW>, dim3(s.grid), dim3(64 * kPrefillW),
+                                    stream, p);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
-    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (s.rows / kMergeRowsPerWG)), dim3(256), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
@@ -760,7 +770,7 @@ hipError_t launch_prefill_causal(const void* q, const void* k, const void* v, vo
 hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* k, float k_scale, const void* v,
                                       float v_scale, void* o, int nq, int n_kv, int q_pos0, int hq, float scale,
                                       void* workspace, hipStream_t stream) {
-  const PrefillSched s = prefill_schedule(nq, hq, q_pos0);
+  const PrefillSched s = prefill_schedule_rows(nq, hq, q_pos0, kRowsPerBlock);  // eight waves of 32 rows
   PrefillParams p;
   p.q = (const _Float16*)q;  // E4M3 codes, read as bytes
   p.k = (const _Float16*)k;
@@ -768,6 +778,7 @@ hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* 
   p.o = (_Float16*)o;
   p.part = (float*)workspace;
   p.nrows = s.nrows;
+  p.qrows = s.rows;
   p.kv_live = q_pos0 + nq;
   (void)n_kv;
   p.q_pos0 = q_pos0;
@@ -783,7 +794,7 @@ hipError_t launch_prefill_causal_e4m3(const void* q, float q_scale, const void* 
   hipError_t e = launch_timed(prefill_causal_e4m3, dim3(s.grid), dim3(512), stream, p);
   if (e != hipSuccess) return e;
   if (prefill_needs_merge(s)) {
-    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (kRowsPerBlock / kMergeRowsPerWG)), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL(prefill_merge, dim3(s.nqb * (s.rows / kMergeRowsPerWG)), dim3(256), 0, stream, p);
     e = hipGetLastError();
   }
   return e;
@@ -814,6 +825,7 @@ hipError_t launch_prefill_causal_varlen(const void* q, const void* k, const void
   p.part = (float*)(ws + varlen_part_offset(vs));
   p.part_bytes = (uint32_t)((size_t)vs.cap * vs.split * kPartialFloats * 4);
   p.nrows = 0;
+  p.qrows = kRowsPerBlock;
   p.kv_live = 0;
   p.q_pos0 = 0;
   p.nqb = vs.cap;

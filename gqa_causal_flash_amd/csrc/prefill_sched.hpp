@@ -13,31 +13,32 @@
 // online-softmax partial (max, sum, unnormalised accumulator) that a second
 // kernel merges exactly by log-sum-exp -- the block partial plus exact merge
 // of the long-prefill page, with the split chosen for an even load on all
-// compute units.
+// compute units.  A workload too small to give every compute unit a
+// workgroup that way takes q-blocks of 128 rows (four waves of 32) instead:
+// twice the workgroups, each with half the matrix-core work per key tile.
 #pragma once
 
 #include <stdint.h>
 
 namespace gqa {
 
-#ifndef GQA_PREFILL_ROWS
-#define GQA_PREFILL_ROWS 256
-#endif
-constexpr int kRowsPerBlock = GQA_PREFILL_ROWS;  // packed rows per workgroup
-constexpr int kWGsPerCU = 1;                     // 128 KiB of LDS per workgroup
+constexpr int kRowsPerBlock = 256;  // packed rows per workgroup
+constexpr int kRowsSmall = 128;     // packed rows per workgroup of small workloads
+constexpr int kWGsPerCU = 1;        // 128 KiB of LDS per workgroup
 constexpr int kTileKeys = 64;       // keys per K/V tile
 constexpr int kTargetGrid = 256;    // one workgroup per MI355X compute unit
 
 struct PrefillSched {
   int nrows;   // nq * hq
   int q_pos0;
+  int rows;    // packed rows per q-block: kRowsPerBlock or kRowsSmall
   int nqb;     // number of q-blocks
   int split;   // pieces per q-block (see below)
   int grid;    // nqb * split workgroups
 };
 
-__host__ __device__ inline int prefill_block_tiles(int b, int nrows, int q_pos0) {
-  int last = (b + 1) * kRowsPerBlock - 1;
+__host__ __device__ inline int prefill_block_tiles(int b, int rows, int nrows, int q_pos0) {
+  int last = (b + 1) * rows - 1;
   if (last > nrows - 1) last = nrows - 1;
   const int pmax = q_pos0 + last / 6;
   return (pmax + kTileKeys) / kTileKeys;  // ceil((pmax + 1) / 64)
@@ -52,14 +53,15 @@ __host__ __device__ inline int prefill_block_tiles(int b, int nrows, int q_pos0)
 // partial in slot b * split + j.  The split is the smallest power of two
 // (<= 8) giving at least two workgroups per compute unit, and never more
 // pieces than the shortest q-block has tiles.
-inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
+inline PrefillSched prefill_schedule_rows(int nq, int hq, int q_pos0, int rows) {
   PrefillSched s;
   s.nrows = nq * hq;
   s.q_pos0 = q_pos0;
-  s.nqb = (s.nrows + kRowsPerBlock - 1) / kRowsPerBlock;
+  s.rows = rows;
+  s.nqb = (s.nrows + rows - 1) / rows;
   int minnt = 1 << 30;
   for (int b = 0; b < s.nqb; ++b) {
-    const int nt = prefill_block_tiles(b, s.nrows, q_pos0);
+    const int nt = prefill_block_tiles(b, rows, s.nrows, q_pos0);
     if (nt < minnt) minnt = nt;
   }
   int sp = 1;
@@ -69,14 +71,33 @@ inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
   return s;
 }
 
-// Partial slot: fp32 acc [64 column quads][rows][4], then m [rows], then l [rows].
-constexpr size_t kPartialFloats = (size_t)kRowsPerBlock * 256 + 2 * kRowsPerBlock;
+// The fp16 kernel's schedule: 256-row q-blocks, or 128-row ones when the
+// 256-row schedule leaves compute units without a workgroup.
+inline PrefillSched prefill_schedule(int nq, int hq, int q_pos0) {
+  const PrefillSched s = prefill_schedule_rows(nq, hq, q_pos0, kRowsPerBlock);
+  return s.grid < kTargetGrid ? prefill_schedule_rows(nq, hq, q_pos0, kRowsSmall) : s;
+}
+
+// Partial slot of a q-block of `rows` packed rows: fp32 acc [64 column
+// quads][rows][4], then m [rows], then l [rows].
+__host__ __device__ constexpr size_t prefill_partial_floats(int rows) { return (size_t)rows * 256 + 2 * (size_t)rows; }
+constexpr size_t kPartialFloats = prefill_partial_floats(kRowsPerBlock);
 
 // True when the q-blocks are cut into pieces whose partials need merging.
 inline bool prefill_needs_merge(const PrefillSched& s) { return s.split > 1; }
 
 inline size_t prefill_workspace_bytes(const PrefillSched& s) {
-  return prefill_needs_merge(s) ? (size_t)s.grid * kPartialFloats * sizeof(float) : 0;
+  return prefill_needs_merge(s) ? (size_t)s.grid * prefill_partial_floats(s.rows) * sizeof(float) : 0;
+}
+
+// One workspace size serves the fp16 kernel's schedule and the E4M3 kernel's,
+// which always takes 256-row q-blocks.  (The 256-row figure is the larger: a
+// 128-row schedule has at most twice the q-blocks, no larger a split and
+// partials of half the size.)
+inline size_t prefill_any_workspace_bytes(int nq, int hq, int q_pos0) {
+  const size_t a = prefill_workspace_bytes(prefill_schedule(nq, hq, q_pos0));
+  const size_t b = prefill_workspace_bytes(prefill_schedule_rows(nq, hq, q_pos0, kRowsPerBlock));
+  return a > b ? a : b;
 }
 
 // Varlen prefill (a batch of sequences packed end to end): the q-blocks of

@@ -45,7 +45,9 @@ def _ws(nq, n_kv, q_pos0, hq=6, hkv=1, d=256):
 def _expected_prefill_workspace(nq, q_pos0, hq=6):
     """The key-split rule restated: q-blocks of 256 packed rows, each cut into the smallest power of two
     (at most 8) of key ranges that gives at least 512 pieces, never more than its shortest q-block has
-    64-key tiles; each piece of a split q-block leaves a 256-row fp32 partial (acc, m, l)."""
+    64-key tiles; each piece of a split q-block leaves a 256-row fp32 partial (acc, m, l).  Workloads
+    whose 256-row schedule has fewer than 256 pieces run 128-row q-blocks, whose partials never need
+    more room (see test_small_workload_schedule_fits_the_workspace)."""
     rows = nq * hq
     nqb = -(-rows // 256)
     tiles = [(q_pos0 + min((b + 1) * 256 - 1, rows - 1) // 6 + 64) // 64 for b in range(nqb)]
@@ -59,6 +61,30 @@ def _expected_prefill_workspace(nq, q_pos0, hq=6):
                                              (777, 2500, 1723), (7, 100, 93), (1, 64, 63), (300, 300, 0)])
 def test_prefill_workspace_follows_the_key_split(nq, n_kv, q_pos0):
     assert _ws(nq, n_kv, q_pos0) == (g.GQA_OK, _expected_prefill_workspace(nq, q_pos0))
+
+
+def _schedule(nq, q_pos0, rows, hq=6):
+    nr = nq * hq
+    nqb = -(-nr // rows)
+    tiles = [(q_pos0 + min((b + 1) * rows - 1, nr - 1) // 6 + 64) // 64 for b in range(nqb)]
+    split = 1
+    while split < 8 and nqb * split < 512 and split * 2 <= min(tiles):
+        split *= 2
+    return nqb, split
+
+
+@pytest.mark.parametrize("nq,q_pos0", [(256, 768), (100, 100), (100, 1000), (40, 40), (43, 64), (1300, 3000),
+                                       (777, 1723), (256, 39744), (1, 0), (7, 93), (300, 0)])
+def test_small_workload_schedule_fits_the_workspace(nq, q_pos0):
+    """Where the fp16 kernel takes 128-row q-blocks (the 256-row schedule has fewer than 256 pieces), the
+    partials of its pieces (128 x 256 + 2 x 128 floats each) fit the workspace the query reports."""
+    nqb, split = _schedule(nq, q_pos0, 256)
+    if nqb * split >= 256:
+        pytest.skip("256-row q-blocks")
+    nqb2, split2 = _schedule(nq, q_pos0, 128)
+    need = 0 if split2 == 1 else nqb2 * split2 * (128 * 256 + 2 * 128) * 4
+    assert _ws(nq, nq + q_pos0, q_pos0) == (g.GQA_OK, _expected_prefill_workspace(nq, q_pos0))
+    assert need <= _expected_prefill_workspace(nq, q_pos0)
 
 
 def test_prefill_workspace_query():

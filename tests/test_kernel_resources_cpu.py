@@ -25,7 +25,8 @@ HIPCC = gbuild.HIPCC
 
 # kernel (demangled prefix) -> (LDS bytes, register budget per lane, scratch bytes allowed)
 EXPECTED = {
-    "prefill_causal_fwd<": (131072, 256, 0),     # 1 workgroup of 8 waves per CU: 2 waves per SIMD
+    "prefill_causal_fwd<1, 8>": (131072, 256, 0),  # 1 workgroup of 8 waves per CU: 2 waves per SIMD
+    "prefill_causal_fwd<1, 4>": (131072, 512, 0),  # 128-row q-blocks: 1 workgroup of 4 waves, 1 wave per SIMD
     "prefill_causal_varlen": (131072, 256, 0),   # same body
     "prefill_causal_e4m3": (98304, 256, 0),
     "prefill_merge": (0, 256, 0),

@@ -29,6 +29,8 @@ def _gpu(q, k, v, q_pos0):
         (64, 1000, 500),    # queries in the middle (keys after them exist)
         (777, 2500, 1723),  # several q-blocks, ragged last block
         (256, 40000, 39744),  # few q-blocks over a long key range: many splits, merge path
+        (1300, 4300, 3000),  # 128-row q-blocks at their largest (the 256-row schedule has 248 pieces)
+        (2100, 4300, 2200),  # 256-row q-blocks (400 pieces), ragged last block, merge path
     ],
 )
 def test_prefill_parity(nq, n_kv, q_pos0):
@@ -59,8 +61,10 @@ def test_prefill_deterministic():
     assert np.array_equal(a, b)
 
 
-# The kernel works on q-blocks of 256 packed rows (token * 6 + head); a test that
-# covers complete q-blocks covers every key-range piece and merge of each.
+# At these sizes the kernel works on q-blocks of 256 packed rows (token * 6 + head);
+# a test that covers complete q-blocks covers every key-range piece and merge of each.
+# (Workloads too small to give every compute unit a piece take 128-row q-blocks:
+# the tiny configuration and most cases of test_prefill_parity.)
 QBLOCK_PACKED_ROWS = 256
 WHOLE_TENSOR_KV = (40000, 128000)  # the page's two printed points (Test Result)
 
