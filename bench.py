@@ -8,6 +8,11 @@ N(0,1) synthetic inputs resident in HBM.  One step is one gqa_prefill_causal
 call (main kernel + log-sum-exp merge).  The metric is algorithmic TFLOP/s:
 4 * D * Hq * (visible query-key pairs) per step over the measured step time.
 
+Every workload runs W warm-up calls, then K timed calls with the library's
+profiling off (the step time), then K more calls with it on (the main
+kernel's time from HIP events, and the shader clock): recording the events
+costs a few microseconds per call, which stays out of the step time.
+
 Prints ONE JSON line.  Besides the driver's fields it carries
   roofline      the dominant kernel's achieved TFLOP/s (algorithmic FLOPs per
                 launch / its average duration, timed with HIP events recorded
@@ -39,7 +44,7 @@ key sweep (Q = 8000 at the last positions of KV = 40000, 48000, ..., 128000),
 each with the step time, the main kernel's time, TFLOP/s and fraction of the
 fp16 peak, and the shader clock; the default single line is not printed then.
 
-Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline] [--sweep]
+Usage: python bench.py [--gpus 1] [--steps K (50)] [--warmup W (3)] [--no-cpu-baseline] [--sweep]
 """
 
 from __future__ import annotations
@@ -176,6 +181,12 @@ def assign_workloads(rows, per: int, n_kv: int):
         yield name, labels[cur][min((count[cur] - 1) // per, len(labels[cur]) - 1)], v
 
 
+def calls_per_workload(steps: int, warmup: int) -> int:
+    """Calls of each kernel that one benchmark workload makes (time_steps): the warm-up calls, the
+    timed steps, and as many profiled calls."""
+    return warmup + 2 * steps
+
+
 def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, calib_mib: int, n_kv: int) -> str:
     """Markdown table of FETCH_SIZE / WRITE_SIZE per launch of every libgqa kernel.
 
@@ -183,7 +194,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
     the known-size reference: each counter's scale factor is the copy's true byte
     count over what the counter reads for it.  Dispatches are assigned to
     workloads by the benchmark's fixed order (assign_workloads)."""
-    per = warmup + steps
+    per = calls_per_workload(steps, warmup)
     true_kib = calib_mib * 1024.0
     result, factors = {}, {}
     for counter, path in (("FETCH_SIZE", fetch_csv), ("WRITE_SIZE", write_csv)):
@@ -212,7 +223,7 @@ def summarize_counters(fetch_csv: str, write_csv: str, steps: int, warmup: int, 
 def summarize_metrics(counter_csv: str, steps: int, warmup: int, n_kv: int) -> str:
     """Markdown table of every counter or derived metric of one rocprofv3 --pmc counter_collection.csv
     of the default benchmark (run with the given --steps/--warmup/--kv), averaged per kernel and workload."""
-    per = warmup + steps
+    per = calls_per_workload(steps, warmup)
     by_counter = {}
     with open(counter_csv, newline="") as f:
         for r in csv.DictReader(f):
@@ -237,8 +248,9 @@ def summarize_metrics(counter_csv: str, steps: int, warmup: int, n_kv: int) -> s
 def summarize_trace(trace_csv: str, steps: int, warmup: int, n_kv: int) -> str:
     """Markdown table of the duration of every libgqa kernel per workload, from a rocprofv3
     --kernel-trace CSV of the default benchmark run with the given --steps/--warmup: average
-    over all dispatches and over the timed ones (the last `steps` of each workload), min, max."""
-    per = warmup + steps
+    over all dispatches and over the timed ones (the 2 * steps after the warm-up of each workload:
+    the timed pass and the profiled pass), min, max."""
+    per = calls_per_workload(steps, warmup)
     rows = []
     with open(trace_csv, newline="") as f:
         for r in csv.DictReader(f):
@@ -252,7 +264,7 @@ def summarize_trace(trace_csv: str, steps: int, warmup: int, n_kv: int) -> str:
     lines = ["| kernel | workload | dispatches | average (us) | timed average (us) | min (us) | max (us) |",
              "|---|---|---|---|---|---|---|"]
     for (name, wl), ds in result.items():
-        timed = ds[-steps:]
+        timed = ds[-2 * steps:]
         lines.append(f"| `{name}` | `{wl}` | {len(ds)} | {sum(ds) / len(ds) / 1e3:,.1f} | "
                      f"{sum(timed) / len(timed) / 1e3:,.1f} | {min(ds) / 1e3:,.1f} | {max(ds) / 1e3:,.1f} |")
     return "\n".join(lines) + "\n"
@@ -262,10 +274,10 @@ def summarize_sweep_trace(trace_csv: str, steps: int, warmup: int) -> str:
     """Markdown table of prefill_causal_fwd / prefill_merge durations per point of the key sweep.
 
     Reads a rocprofv3 --kernel-trace CSV of `bench.py --sweep --steps S --warmup W`: the sweep runs its
-    points in order (KV = 40000, 48000, ..., 128000), each with warmup + steps calls, so dispatch i of a
-    kernel belongs to point i // (warmup + steps).  The timed calls' kernel time is the average over the
-    last `steps` dispatches of each point."""
-    per = warmup + steps
+    points in order (KV = 40000, 48000, ..., 128000), each with calls_per_workload(S, W) calls, so
+    dispatch i of a kernel belongs to point i // calls_per_workload(S, W).  The timed calls' kernel time
+    is the average over the dispatches after the warm-up of each point."""
+    per = calls_per_workload(steps, warmup)
     points = (workloads.LONG_40K,) + workloads.SWEEP
     dur = {"prefill_causal_fwd": [], "prefill_merge": []}
     with open(trace_csv, newline="") as f:
@@ -316,9 +328,13 @@ def numpy_blas() -> str:
 
 
 def time_steps(fn, steps: int, warmup: int):
-    """Run fn warmup times, then time exactly `steps` calls (sync on both sides).
+    """Run fn warmup times, then time exactly `steps` calls (sync on both sides) with the library's
+    profiling off: the wall time per step.  Then run `steps` more calls with profiling on: the main
+    kernel's time per launch from the timing-only HIP events the library records around it on the
+    call's stream, and the shader clock its workgroups sample.  Recording the events costs a few
+    microseconds per call, so they stay out of the step time.
 
-    Returns (wall ms per step, main-kernel ms per launch from library events)."""
+    Returns (wall ms per step, main-kernel ms per launch); the clock is left in time_steps.clock_mhz."""
     import torch
 
     import gqa_causal_flash_amd as g
@@ -326,12 +342,15 @@ def time_steps(fn, steps: int, warmup: int):
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
-    g.gqa_profile_start()
     t0 = time.perf_counter()
     for _ in range(steps):
         fn()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
+    g.gqa_profile_start()
+    for _ in range(steps):
+        fn()
+    torch.cuda.synchronize()
     kms, kn = g.gqa_profile_stop()
     time_steps.clock_mhz = g.gqa_profile_clock_mhz()
     return wall, (kms / kn if kn else float("nan"))
@@ -629,7 +648,8 @@ def bench_verify(nq, steps, warmup, copies=3, seed=0):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
+    # 50 timed steps: the short paths (tens of microseconds per step) then average over a few ms per pass
+    ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)

@@ -21,11 +21,12 @@ def _k(name):
 def test_summarize_counters_scales_and_assigns_workloads(tmp_path, monkeypatch):
     copy = "__amd_rocclr_copyBuffer"
     # 1 MiB calibration; FETCH reads half the true size (scale 2), WRITE the true size (scale 1)
-    fetch = [(copy, 512.0)] * 3 + [(_k("prefill_causal_fwd"), 100.0), (_k("prefill_merge"), 10.0)] * 2
+    per = bench.calls_per_workload(steps=1, warmup=1)  # warm-up, timed and profiled call
+    fetch = [(copy, 512.0)] * 3 + [(_k("prefill_causal_fwd"), 100.0), (_k("prefill_merge"), 10.0)] * per
     for s in range(3):
-        fetch += [(_k("paged_prepass"), 1.0), (_k("paged_fwd"), 20.0 + s)] * 2
+        fetch += [(_k("paged_prepass"), 1.0), (_k("paged_fwd"), 20.0 + s)] * per
     for q in range(len(bench.VERIFY_QUERIES)):
-        fetch += [(_k("verify_fwd"), 30.0 + q), (_k("verify_merge"), 3.0)] * 2
+        fetch += [(_k("verify_fwd"), 30.0 + q), (_k("verify_merge"), 3.0)] * per
     write = [(n, 2 * v if n == copy else v / 2) for n, v in fetch]
     _write_counters(tmp_path / "f.csv", "FETCH_SIZE", fetch)
     _write_counters(tmp_path / "w.csv", "WRITE_SIZE", write)
@@ -59,7 +60,8 @@ def test_committed_traffic_table_parses():
 
 
 def test_summarize_sweep_trace_assigns_points_in_order(tmp_path):
-    """Dispatch i of a kernel belongs to sweep point i // (warmup + steps); only the timed ones are averaged."""
+    """Dispatch i of a kernel belongs to sweep point i // calls_per_workload; only the calls after the
+    warm-up (timed and profiled passes) are averaged."""
     import workloads
 
     points = (workloads.LONG_40K,) + workloads.SWEEP
@@ -71,7 +73,7 @@ def test_summarize_sweep_trace_assigns_points_in_order(tmp_path):
         w.writeheader()
         t = 0
         for i in range(len(points)):
-            for j in range(warmup + steps):
+            for j in range(bench.calls_per_workload(steps, warmup)):
                 fwd = 10**9 if j < warmup else (i + 1) * 10**6 + j  # warm-up calls are slow and must be ignored
                 w.writerow({"Kernel_Name": _k("prefill_causal_fwd"), "Start_Timestamp": t, "End_Timestamp": t + fwd})
                 t += fwd
@@ -82,5 +84,5 @@ def test_summarize_sweep_trace_assigns_points_in_order(tmp_path):
     for i, (cfg, row) in enumerate(zip(points, rows)):
         cells = [c.strip() for c in row.strip("|").split("|")]
         assert int(cells[0]) == cfg.n_kv
-        assert float(cells[3]) == round(((i + 1) * 10**6 + 1.5) / 1e6, 4)  # mean of j = 1, 2
+        assert float(cells[3]) == round(((i + 1) * 10**6 + 2.5) / 1e6, 4)  # mean of j = 1 .. 4
         assert float(cells[7]) == 30.0
