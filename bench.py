@@ -44,7 +44,7 @@ key sweep (Q = 8000 at the last positions of KV = 40000, 48000, ..., 128000),
 each with the step time, the main kernel's time, TFLOP/s and fraction of the
 fp16 peak, and the shader clock; the default single line is not printed then.
 
-Usage: python bench.py [--gpus 1] [--steps K (50)] [--warmup W (3)] [--no-cpu-baseline] [--sweep]
+Usage: python bench.py [--gpus 1] [--steps K (50)] [--warmup W (20)] [--no-cpu-baseline] [--sweep]
 """
 
 from __future__ import annotations
@@ -650,7 +650,8 @@ def main(argv=None):
     ap.add_argument("--gpus", type=int, default=1)
     # 50 timed steps: the short paths (tens of microseconds per step) then average over a few ms per pass
     ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=3)
+    # the card takes tens of launches to settle (the first long prefills run up to 15 % slower)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--kv", type=int, default=workloads.HEADLINE.n_kv, help="key count of the prefill workload")

@@ -201,6 +201,8 @@ __device__ __forceinline__ void store_rows_f16(rsrc_t ro, int row, int half, con
 // Online-softmax partial of one column block for a later log-sum-exp merge.
 // Slot layout (fp32): acc[64 column quads][rows_per_slot rows][4], then
 // m[rows_per_slot], then l[rows_per_slot].  `rl` is the row inside the slot.
+// The accumulator goes out written through (store_16B_through): lanes 0..31
+// and 32..63 each write 512 contiguous bytes.
 __device__ __forceinline__ void store_partial(rsrc_t rp, uint32_t slot_byte, int rows_per_slot, int rl, int half,
                                               const f16x (&acc)[8], float m, float lt) {
 #pragma unroll
@@ -209,7 +211,7 @@ __device__ __forceinline__ void store_partial(rsrc_t rp, uint32_t slot_byte, int
     for (int g = 0; g < 4; ++g) {
       const int quad = 8 * dt + 2 * g + half;  // columns 4*quad .. 4*quad+3
       const f4 x = {acc[dt][4 * g], acc[dt][4 * g + 1], acc[dt][4 * g + 2], acc[dt][4 * g + 3]};
-      store_16B(rp, slot_byte + (uint32_t)((quad * rows_per_slot + rl) * 16), __builtin_bit_cast(u4, x));
+      store_16B_through(rp, slot_byte + (uint32_t)((quad * rows_per_slot + rl) * 16), __builtin_bit_cast(u4, x));
     }
   if (half == 0) {
     const uint32_t mo = slot_byte + (uint32_t)(rows_per_slot * kHeadDim * 4);
