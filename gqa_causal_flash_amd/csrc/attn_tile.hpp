@@ -63,6 +63,34 @@ __device__ __forceinline__ void qk_32keys_f(KFrag kfrag, const h8 (&qf)[C][16], 
   }
 }
 
+// qk_32keys_f with memory copies interleaved: hook(i), i = 0..7, issues one
+// vector-memory instruction after product 2i, so that a wave's copies reach
+// the vector-memory pipe spread over its products instead of in one burst.
+template <int C, int KPF, class KFrag, class Hook>
+__device__ __forceinline__ void qk_32keys_fh(KFrag kfrag, const h8 (&qf)[C][16], f16x (&s)[C], Hook hook) {
+#pragma unroll
+  for (int c = 0; c < C; ++c) s[c] = f16x{};
+  constexpr int kPF = KPF;
+  h8 kf[kPF];
+#pragma unroll
+  for (int j = 0; j < kPF; ++j) kf[j] = kfrag(j);
+#pragma unroll
+  for (int si = 0; si < 16; ++si) {
+    const h8 a = kf[si % kPF];
+    if (si + kPF < 16) kf[si % kPF] = kfrag(si + kPF);
+#pragma unroll
+    for (int c = 0; c < C; ++c) s[c] = mfma(a, qf[c][si], s[c]);
+    if (si % 2 == 0) hook(si / 2);
+  }
+  __builtin_amdgcn_sched_group_barrier(0x100, kPF, 0);
+#pragma unroll
+  for (int si = 0; si < 16; ++si) {
+    __builtin_amdgcn_sched_group_barrier(0x008, C, 0);
+    if (si + kPF < 16) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+    if (si % 2 == 0) __builtin_amdgcn_sched_group_barrier(0x010, 1, 0);
+  }
+}
+
 // S^T[32 keys][32C rows] = K Q^T for keys 32kb .. 32kb+31 of the staged tile.
 template <int C, int KPF = GQA_KPF>
 __device__ __forceinline__ void qk_32keys(uint32_t kaddr, int kb, const h8 (&qf)[C][16], f16x (&s)[C]) {
@@ -166,13 +194,14 @@ __device__ __forceinline__ void attend_32keys(uint32_t kaddr, const GQA_LDS char
 // attend_32keys for the first 32 keys of a K tile named by its LDS pointer `kt`
 // (bk = k_lane_base of the lane): the fragment addresses keep the tile's
 // identity, so the compiler can tell the tile apart from LDS that loads are
-// landing in elsewhere.
-template <int C, class Visible, int KPF = GQA_KPF, int KPV = GQA_KPV>
+// landing in elsewhere.  hook(i), i = 0..7, issues one vector-memory copy
+// among the Q K^T products (qk_32keys_fh).
+template <int C, class Visible, int KPF, int KPV, class Hook>
 __device__ __forceinline__ void attend_32keys_p(const GQA_LDS char* kt, uint32_t bk, const GQA_LDS char* vt, uint32_t bv,
                                                 const h8 (&qf)[C][16], f16x (&acc)[C][8], float (&m)[C],
-                                                float (&l)[C], float cscale, bool mask, Visible visible) {
+                                                float (&l)[C], float cscale, bool mask, Visible visible, Hook hook) {
   f16x s[C];
-  qk_32keys_f<C, KPF>([&](int si) { return *(const GQA_LDS h8*)(kt + (bk ^ (32u * (uint32_t)si))); }, qf, s);
+  qk_32keys_fh<C, KPF>([&](int si) { return *(const GQA_LDS h8*)(kt + (bk ^ (32u * (uint32_t)si))); }, qf, s, hook);
   h8 pk[C][2];
   softmax_32keys<C>(s, acc, m, l, cscale, mask, visible, pk);
   pv_32keys<C, KPV>(vt, bv, 0, pk, acc);

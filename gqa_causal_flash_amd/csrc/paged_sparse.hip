@@ -21,7 +21,9 @@
 //   paged_fwd      teams of three workgroups (one per 128-row group of a query
 //                  block) over runs of equal cost: gathers 8 blocks (32 keys)
 //                  per sub-tile into swizzled double-buffered LDS tiles with
-//                  direct-to-LDS loads, records each key's logical position,
+//                  direct-to-LDS loads (each wave's eight copies spread over
+//                  the Q K^T products of the sub-tile before), records each
+//                  key's logical position,
 //                  and runs the shared 32-key step with the mask "position <=
 //                  query position".  The padding slots of a query block's
 //                  last sub-tile are fetched at an offset past the end of the
@@ -492,29 +494,46 @@ __device__ __forceinline__ SubEntries sub_entries(const int2* ent, int e0, int e
   return s;
 }
 
-__device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk, rsrc_t rv, const SubEntries& se,
-                                                char* kdst, char* vdst, int* kpos, int wave, int lane, uint32_t kl,
-                                                uint32_t vl) {
+// Copy i (0..7) of the wave's share of a sub-tile: K (i even) or V (i odd)
+// rows 8w + 2c, 8w + 2c + 1 with c = i / 2.  With `more` false the copy reads
+// zeros (the offset is past the cache), which keeps every copy unconditional.
+__device__ __forceinline__ void paged_issue_copy(const PagedParams& p, rsrc_t rk, rsrc_t rv, const SubEntries& se,
+                                                 char* kdst, char* vdst, int wave, int lane, uint32_t kl, uint32_t vl,
+                                                 int i, bool more) {
   const int half = lane >> 5;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int2 en = se.e[i / 2];
-    const int u = 2 * (i & 1) + half;
-    const bool live = en.x >= 0 && en.y + u < p.live_len;
-    const uint32_t j = (uint32_t)(4 * (wave & 1) + i);
-    const uint32_t base = (uint32_t)(en.x + u) * kRowBytes - (uint32_t)(2 * i + half) * kRowBytes;
-    const uint32_t vk = live ? base + (kl ^ (32u * j)) + 1024u * i : kNoRow;
-    const uint32_t vv = live ? base + (vl ^ (128u * (j & 3))) + 1024u * i : kNoRow;
-    const int r0 = 8 * wave + 2 * i;
+  const int c = i >> 1;
+  const int2 en = se.e[c / 2];
+  const int u = 2 * (c & 1) + half;
+  const bool live = more && en.x >= 0 && en.y + u < p.live_len;
+  const uint32_t j = (uint32_t)(4 * (wave & 1) + c);
+  const uint32_t base = (uint32_t)(en.x + u) * kRowBytes - (uint32_t)(2 * c + half) * kRowBytes;
+  const int r0 = 8 * wave + 2 * c;
+  if ((i & 1) == 0) {
+    const uint32_t vk = live ? base + (kl ^ (32u * j)) + 1024u * c : kNoRow;
     load_lds_16B(rk, (GQA_LDS char*)(kdst + r0 * kRowBytes), vk, 0);
+  } else {
+    const uint32_t vv = live ? base + (vl ^ (128u * (j & 3))) + 1024u * c : kNoRow;
     load_lds_16B(rv, (GQA_LDS char*)(vdst + r0 * kRowBytes), vv, 0);
   }
+}
+
+// Lanes 0..7 record the logical position of row 8w + l of the sub-tile.
+__device__ __forceinline__ void paged_stage_pos(const PagedParams& p, const SubEntries& se, int* kpos, int wave,
+                                                int lane) {
   if (lane < 8) {
     const int2 en = lane < 4 ? se.e[0] : se.e[1];
     const int u = lane & 3;
     const bool live = en.x >= 0 && en.y + u < p.live_len;
     kpos[8 * wave + lane] = live ? en.y + u : kDeadToken;
   }
+}
+
+__device__ __forceinline__ void paged_issue_sub(const PagedParams& p, rsrc_t rk, rsrc_t rv, const SubEntries& se,
+                                                char* kdst, char* vdst, int* kpos, int wave, int lane, uint32_t kl,
+                                                uint32_t vl) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) paged_issue_copy(p, rk, rv, se, kdst, vdst, wave, lane, kl, vl, i, true);
+  paged_stage_pos(p, se, kpos, wave, lane);
 }
 
 __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
@@ -618,8 +637,12 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
     auto step = [&](auto ic, int x) {
       constexpr int I = decltype(ic)::value;  // (x - s0) % 2
       const bool mask = x >= x_mask;
-      if (x + 1 < s1) issue(std::integral_constant<int, I ^ 1>{}, es[I ^ 1]);  // lands in the other slot
-      es[I ^ 1] = sub_entries(ent, e_beg + 8 * (x + 3), e_end, wave);          // used two steps on
+      // the gather of x + 1 lands in the other slot: its positions are staged
+      // here and its eight copies go out among the Q K^T products
+      const bool more = x + 1 < s1;
+      const SubEntries nxt = es[I ^ 1];
+      if (more) paged_stage_pos(p, nxt, pslot(std::integral_constant<int, I ^ 1>{}), wave, lane);
+      es[I ^ 1] = sub_entries(ent, e_beg + 8 * (x + 3), e_end, wave);  // used two steps on
       // keep the per-lane bases opaque so derived addresses are formed here,
       // next to their use, instead of being hoisted and held in registers
       asm volatile("" : "+v"(bk), "+v"(bv));
@@ -629,7 +652,12 @@ __global__ __launch_bounds__(256, 2) void paged_fwd(PagedParams p) {
       // schedule state, and no value of the loop is spilled
       attend_32keys_p<1, decltype(visible), 2, 2>((const GQA_LDS char*)kslot(std::integral_constant<int, I>{}), bk,
                                                   (const GQA_LDS char*)vslot(std::integral_constant<int, I>{}), bv, qf,
-                                                  acc, m, l, p.c, mask, visible);
+                                                  acc, m, l, p.c, mask, visible, [&](int i) {
+                                                    paged_issue_copy(p, rk, rv, nxt,
+                                                                     kslot(std::integral_constant<int, I ^ 1>{}),
+                                                                     vslot(std::integral_constant<int, I ^ 1>{}), wave,
+                                                                     lane, kl, vl, i, more);
+                                                  });
       // the gather into the other slot has landed and every wave is done with
       // this one (a barrier without a memory fence: the wait is explicit)
       __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
