@@ -131,6 +131,7 @@ __global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
     loff[j] = (uint32_t)r * kFp8Row + 16u * ((uint32_t)(lane & 15) ^ swz);
   }
   const uint32_t ldst = (stage_v ? kRawTile : 0) + 1024u * (uint32_t)(i0 & 7);
+  const uint32_t kv_bytes = (uint32_t)p.n_kv * kFp8Row;
   auto issue = [&](char* slot, int t) {  // this wave's pieces of tile t into a slot
     GQA_LDS char* dst = (GQA_LDS char*)slot + ldst;
 #pragma unroll
@@ -170,7 +171,7 @@ __global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
   uint32_t vbase = (uint32_t)vrow0 * kFp8Row + 8u * (sk & 1);
 
   // one 32-key tile t from the raw K bytes at kt (V bytes follow)
-  auto compute = [&](const GQA_LDS char* kt, int t) {
+  auto compute = [&](const GQA_LDS char* kt, int t, auto hook) {
     const GQA_LDS char* vt = kt + kRawTile;
     const int k0 = t * kVTileKeys;
     asm volatile("" : "+v"(kbase), "+v"(vbase));
@@ -182,6 +183,7 @@ __global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
       const uint32_t ch = (uint32_t)(8 * half + (si >> 1)) ^ k_swz(col);
       const v2i raw = *(const GQA_LDS v2i*)(kt + kbase + 16u * ch + 8u * (si & 1));
       s1[0] = mfma(decode8(raw), qf[0][si], s1[0]);
+      hook(si);
     }
     h8 pk[1][2];
     softmax_32keys<1>(s1, acc, m, l, p.c, k0 + 31 > pos_min,
@@ -201,7 +203,9 @@ __global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
   // (parity 0) and 2s + 1 (parity 1).  Three tiles are issued up front; step
   // s waits for tiles 2s and 2s + 1 with tile 2s + 2 still in flight, then
   // issues tiles 2s + 3 and 2s + 4 into the slots of tiles 2s - 2 and 2s - 1,
-  // which every wave finished in step s - 1.
+  // which every wave finished in step s - 1.  Those copies go out spread over
+  // the Q K^T products of the step's own tile, not in one burst (each copy
+  // sets M0, which keeps them in issue order for the counted waits).
 #pragma unroll
   for (int j = 0; j < 3; ++j)
     if (j < n) issue(ring.s[j], t_lo + j);
@@ -221,9 +225,32 @@ __global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
         asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       }
       lds_barrier();
-      if (2 * st + 3 < n) issue(ring.s[(2 * S + 3) % kRing], t_lo + 2 * st + 3);
-      if (2 * st + 4 < n) issue(ring.s[(2 * S + 4) % kRing], t_lo + 2 * st + 4);
-      if (2 * st + PAR < n) compute((const GQA_LDS char*)ring.s[(2 * S + PAR) % kRing], t_lo + 2 * st + PAR);
+      // a tile past the range reads from a resource of no bytes: nothing is
+      // fetched, and the idle slot it names fills with zeros
+      const rsrc_t r3 = make_rsrc(stage_v ? (const void*)p.v : (const void*)p.k, 2 * st + 3 < n ? kv_bytes : 0u);
+      const rsrc_t r4 = make_rsrc(stage_v ? (const void*)p.v : (const void*)p.k, 2 * st + 4 < n ? kv_bytes : 0u);
+      GQA_LDS char* d3 = (GQA_LDS char*)ring.s[(2 * S + 3) % kRing] + ldst;
+      GQA_LDS char* d4 = (GQA_LDS char*)ring.s[(2 * S + 4) % kRing] + ldst;
+      const uint32_t o3 = (uint32_t)(t_lo + 2 * st + 3) * kRawTile, o4 = o3 + kRawTile;
+      auto one = [&](int q) {
+        if (q < kLoads)
+          load_lds_16B(r3, d3 + q * 1024, loff[q], o3);
+        else
+          load_lds_16B(r4, d4 + (q - kLoads) * 1024, loff[q - kLoads], o4);
+      };
+      if (2 * st + PAR < n) {
+        compute((const GQA_LDS char*)ring.s[(2 * S + PAR) % kRing], t_lo + 2 * st + PAR, [&](int si) {
+          if constexpr (2 * kLoads >= 16) {
+#pragma unroll
+            for (int q = si * (2 * kLoads / 16); q < (si + 1) * (2 * kLoads / 16); ++q) one(q);
+          } else {
+            if (si % (16 / (2 * kLoads)) == 0) one(si / (16 / (2 * kLoads)));
+          }
+        });
+      } else {
+#pragma unroll
+        for (int q = 0; q < 2 * kLoads; ++q) one(q);
+      }
     };
     for (int st = 0; 2 * st < n; st += kRing) {
       step(std::integral_constant<int, 0>{}, st);
@@ -249,6 +276,7 @@ __global__ __launch_bounds__(128 * RB, 2) void verify_fwd(VerifyParams p) {
   // b sits in ring slot 2b + j / 64 at float (j % 64) * 64 + lane; m and l in
   // slot 4 at float (2b + {0, 1}) * 64 + lane.
   float lt = swap_halves_sum(l[0]);
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // no copy is still landing in the ring
   lds_barrier();  // every wave is done with the ring
   auto hand = [&](auto rbc, bool write) {
     constexpr int B = decltype(rbc)::value;
